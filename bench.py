@@ -1,0 +1,248 @@
+"""Benchmark of the GDN layer hot path on one MI355X.
+
+One step = one pass of every path of the layer on synthetic inputs resident in HBM:
+  * chunked prefill of one sequence of T = 8192 tokens (16 k-heads, 48 v-heads,
+    d = 128, conv width 4, bf16 inputs, fp32 state, zero initial state);
+  * one decode step on 4 slots (same geometry, states ~ N(0, 0.02));
+  * verify of k = 4 drafts on 4 slots, then rollback to seeded accepted lengths.
+
+Decode and verify rotate through enough slot pools (32 x 24 MiB) that no call
+finds its state in the 256 MB last-level cache left by an earlier call.
+
+Output: one JSON line.  `value` is prefill tokens per second over whole steps
+(T tokens per step, decode and verify included in the step time).  Extra keys
+give per-path figures measured with HIP events on the launch stream: prefill
+alone, decode state GB/s, verify GB/s, and the roofline fraction of each.
+The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+
+T_PREFILL = 8192
+# algorithmic work (per-unit figures of the layer at d = 128, H_v = 48, G = 3, chunk 64)
+PREFILL_FLOP_PER_TOKEN = 7_667_712            # 48 v-heads x 159 744
+PREFILL_BYTES_PER_TOKEN = 20480 + 192 + 12288  # x, a+b, o (bf16)
+DECODE_BYTES = 26_116_864                      # cfg: 4 slots x 1 token
+DECODE_STATE_BYTES = 25_165_824                # state read + write
+VERIFY_BYTES = 64_752_640                      # 4 slots x k = 4, snapshots written
+ROLLBACK_BYTES_PER_SLOT = 6_291_456
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--pools", type=int, default=32)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=1024,
+                   help="prefix of the prefill sequence the CPU oracle runs on")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the layer's multi-GPU "
+                                   "sharding is a design note, not a measured path", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_delta_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    bf = torch.bfloat16
+    g = gi.GEOM_QWEN
+    geom = gdn.Geometry()
+
+    # ---------------- inputs (seeded, resident in HBM) ----------------
+    pin = gi.workload(3)
+    xp = torch.from_numpy(pin["x"]).to(bf).to(dev)
+    ap = torch.from_numpy(pin["a"]).to(bf).to(dev)
+    bp = torch.from_numpy(pin["b"]).to(bf).to(dev)
+    cw = torch.from_numpy(pin["conv_w"]).to(dev)
+    cu = torch.from_numpy(pin["cu_seqlens"]).to(dev)
+    pslot = torch.from_numpy(pin["slots"]).to(dev)
+    phas = torch.from_numpy(pin["has_init"]).to(dev)
+    ppool = gdn.SlotPool.zeros(geom)
+    po = torch.empty(T_PREFILL, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    ws = gdn.alloc_prefill_workspace(geom, T_PREFILL, 1)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    dinp = gi.workload(2)
+    vinp = gi.workload(5)
+    pools = []
+    for i in range(args.pools):
+        pl = gdn.SlotPool.zeros(geom)
+        pl.state.normal_(0.0, 0.02)
+        pl.conv_state.normal_(0.0, 0.1)
+        pools.append(pl)
+    dx = torch.from_numpy(dinp["x"][:, 0]).to(bf).to(dev)
+    da = torch.from_numpy(dinp["a"][:, 0]).to(bf).to(dev)
+    db = torch.from_numpy(dinp["b"][:, 0]).to(bf).to(dev)
+    dslot = torch.from_numpy(dinp["slots"]).to(dev)
+    do = torch.empty(4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    vx = torch.from_numpy(vinp["x"]).to(bf).to(dev)
+    va = torch.from_numpy(vinp["a"]).to(bf).to(dev)
+    vb = torch.from_numpy(vinp["b"]).to(bf).to(dev)
+    vslot = torch.from_numpy(vinp["slots"]).to(dev)
+    vacc = torch.from_numpy(vinp["accepted"]).to(dev)
+    snap = torch.empty(4, 4, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+    vo = torch.empty(4, 4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(i, rec=None):
+        pl = pools[i % len(pools)]
+        pl2 = pools[(i + len(pools) // 2) % len(pools)]
+        e = [ev() for _ in range(5)] if rec is not None else None
+        if e: e[0].record(stream)
+        gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err)
+        if e: e[1].record(stream)
+        gdn.decode_step(geom, pl, dx, da, db, cw, dslot, do, dev_err=err)
+        if e: e[2].record(stream)
+        gdn.verify_k(geom, pl2, vx, va, vb, cw, vslot, snap, vo, dev_err=err)
+        if e: e[3].record(stream)
+        gdn.rollback(geom, pl2, snap, vslot, vacc, dev_err=err)
+        if e: e[4].record(stream)
+        if rec is not None:
+            rec.append(e)
+
+    # ---------------- warmup + validity gate ----------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        print(json.dumps({"error": f"device error code {int(err.item())} during warmup"}))
+        sys.exit(3)
+    # validity gate without the oracle: the decode path replayed over the first
+    # 64 tokens of the sequence must reproduce the prefill's outputs
+    gpool = gdn.SlotPool.zeros(geom)
+    gslot = torch.zeros(1, dtype=torch.int32, device=dev)
+    go = torch.empty(1, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    n_chk = 64
+    rep = torch.empty(n_chk, g.n_v_heads, g.d_v, dtype=torch.float32, device=dev)
+    for t in range(n_chk):
+        gdn.decode_step(geom, gpool, xp[t:t + 1], ap[t:t + 1], bp[t:t + 1], cw, gslot, go, dev_err=err)
+        rep[t] = go[0].float()
+    torch.cuda.synchronize()
+    ref = rep.cpu().numpy()
+    got = po[:n_chk].float().cpu().numpy()
+    consistency = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    if not (np.isfinite(got).all() and consistency <= 2e-2):
+        print(json.dumps({"error": f"prefill/decode consistency gate failed: rel err {consistency:.3e}"}))
+        sys.exit(4)
+
+    # ---------------- timed region ----------------
+    rec = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start, e_end = ev(), ev()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, rec)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e_start.elapsed_time(e_end)
+    if int(err.item()) != 0:
+        print(json.dumps({"error": f"device error code {int(err.item())} in timed steps"}))
+        sys.exit(3)
+
+    def avg_ms(a, b):
+        return float(np.mean([r[a].elapsed_time(r[b]) for r in rec]))
+
+    ms_prefill = avg_ms(0, 1)
+    ms_decode = avg_ms(1, 2)
+    ms_verify = avg_ms(2, 3)
+    ms_rollback = avg_ms(3, 4)
+    ms_step = gpu_ms / args.steps
+    if min(ms_prefill, ms_decode, ms_verify, ms_step) <= 0:
+        print(json.dumps({"error": "a timing came out as zero"}))
+        sys.exit(5)
+
+    value = T_PREFILL / (ms_step * 1e-3)
+    prefill_tflops = PREFILL_FLOP_PER_TOKEN * T_PREFILL / (ms_prefill * 1e-3) / 1e12
+    decode_gbs = DECODE_BYTES / (ms_decode * 1e-3) / 1e9
+    decode_state_gbs = DECODE_STATE_BYTES / (ms_decode * 1e-3) / 1e9
+    verify_gbs = VERIFY_BYTES / (ms_verify * 1e-3) / 1e9
+    n_acc = int((vinp["accepted"] > 0).sum())
+    rollback_gbs = ROLLBACK_BYTES_PER_SLOT * n_acc / (ms_rollback * 1e-3) / 1e9
+
+    out = {
+        "metric": "GDN layer prefill tokens/s (T=8192) + decode state GB/s vs HBM peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn layer: prefill T=8192 + decode 4 slots + verify/rollback 4x4",
+                   "n_k_heads": 16, "n_v_heads": 48, "d_k": 128, "d_v": 128, "conv_width": 4,
+                   "chunk": 64, "seq_len": T_PREFILL, "decode_slots": 4, "verify_k": 4,
+                   "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gdn_prefill_chunked (plan + chunk + state kernels)",
+                     "achieved": round(prefill_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "prefill": {"ms": round(ms_prefill, 4), "tokens_per_s": round(T_PREFILL / (ms_prefill * 1e-3), 1),
+                    "tflops": round(prefill_tflops, 2),
+                    "hbm_gbs_algorithmic": round(PREFILL_BYTES_PER_TOKEN * T_PREFILL / (ms_prefill * 1e-3) / 1e9, 1),
+                    "decode_replay_rel_err_64": consistency},
+        "decode": {"us": round(ms_decode * 1e3, 2), "state_gbs": round(decode_state_gbs, 1),
+                   "total_gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
+                   "cold_pools": len(pools)},
+        "verify": {"us": round(ms_verify * 1e3, 2), "gbs": round(verify_gbs, 1),
+                   "frac_hbm_peak": round(verify_gbs / HBM_PEAK_GBS, 4)},
+        "rollback": {"us": round(ms_rollback * 1e3, 2), "gbs": round(rollback_gbs, 1), "slots_copied": n_acc},
+        "wall_s": round(wall, 3),
+    }
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    # (the only place the benchmark touches the oracle; its outputs double as a
+    # parity check of the GPU prefill on the same tokens)
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import gdn_oracle as orc
+        n = args.cpu_tokens
+        with threadpool_limits(1):
+            c0 = time.perf_counter()
+            o_ref, _, _ = orc.layer_sequence(g, pin["x"][:n], pin["a"][:n], pin["b"][:n], pin["conv_w"],
+                                             np.zeros((g.n_v_heads, 128, 128)), np.zeros((3, g.conv_channels)))
+            cs = time.perf_counter() - c0
+        got = po[:n].float().cpu().numpy()
+        parity = float(np.max(np.abs(got - o_ref)) / np.max(np.abs(o_ref)))
+        if not parity <= 2e-2:
+            print(json.dumps({"error": f"prefill parity vs oracle failed: rel err {parity:.3e}"}))
+            sys.exit(4)
+        out["prefill"]["parity_rel_err_vs_oracle"] = parity
+        out["cpu_baseline"] = {"value": round(n / cs, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"fp64 oracle, first {n} tokens of the T=8192 prefill, all 48 v-heads, "
+                                         f"{cs:.1f} s on one host core"}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

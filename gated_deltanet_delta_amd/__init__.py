@@ -1,0 +1,303 @@
+"""Gated DeltaNet layer for AMD MI355X (gfx950): Python binding of libgdn.so.
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices on the host (so that no kernel is launched on buffers smaller than
+its grid assumes), then passes raw device pointers and the current HIP stream
+to the C ABI declared in include/gdn.h.  Every step of the layer runs in the
+library's HIP kernels; there is no fallback.  If libgdn.so has not been built
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32 = 0
+GDN_BF16 = 1
+GDN_FLAG_L2NORM_QK = 1
+POS_ONE = 65536
+CHUNK = 64
+
+DEV_OK = 0
+DEV_BAD_SLOT = 1
+DEV_BAD_ACCEPTED = 2
+DEV_BAD_SEQLENS = 3
+
+
+class GdnGeometry(ctypes.Structure):
+    _fields_ = [
+        ("n_k_heads", ctypes.c_int32),
+        ("n_v_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32),
+        ("conv_channels", ctypes.c_int32),
+        ("conv_ring", ctypes.c_int32),
+        ("max_draft", ctypes.c_int32),
+        ("n_slots", ctypes.c_int32),
+        ("dtype_in", ctypes.c_int32),
+        ("dtype_out", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("q_scale", ctypes.c_float),
+        ("l2_eps", ctypes.c_float),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+        self.message = message
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_version": (ctypes.c_char_p, []),
+    "gdn_check_geometry": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), ctypes.c_char_p, ctypes.c_size_t]),
+    "gdn_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GdnGeometry), _I, _I]),
+    "gdn_conv_state_step": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "gdn_decode_step": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                       _P, _P, _P]),
+    "gdn_prefill_chunked": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P, _P]),
+    "gdn_verify_k": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                    _P, _P, _P, _P]),
+    "gdn_rollback": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _I, _P, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m gated_deltanet_delta_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise GdnError(status, L.gdn_status_string(status).decode(), L.gdn_last_error().decode())
+
+
+# --------------------------------------------------------------------------
+# geometry
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Geometry:
+    """Python mirror of gdn_geometry (see include/gdn.h for every field)."""
+
+    n_k_heads: int = 16
+    n_v_heads: int = 48
+    d_k: int = 128
+    d_v: int = 128
+    conv_width: int = 4
+    conv_ring: int = 8
+    max_draft: int = 4
+    n_slots: int = 8
+    dtype: torch.dtype = torch.bfloat16
+    l2norm_qk: bool = True
+    q_scale: float = 1.0
+    l2_eps: float = 1e-6
+
+    @property
+    def conv_channels(self) -> int:
+        return 2 * self.n_k_heads * self.d_k + self.n_v_heads * self.d_v
+
+    def c_struct(self) -> GdnGeometry:
+        code = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}[self.dtype]
+        return GdnGeometry(self.n_k_heads, self.n_v_heads, self.d_k, self.d_v, self.conv_width,
+                           self.conv_channels, self.conv_ring, self.max_draft, self.n_slots, code, code,
+                           GDN_FLAG_L2NORM_QK if self.l2norm_qk else 0, self.q_scale, self.l2_eps)
+
+    def check(self):
+        g = self.c_struct()
+        _check(lib().gdn_check_geometry(ctypes.byref(g), None, 0))
+
+
+# --------------------------------------------------------------------------
+# host-side marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: missing")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, required {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, required {tuple(shape)}")
+
+
+@dataclass
+class SlotPool:
+    """Caller-owned device buffers of one layer's slot pool."""
+
+    state: torch.Tensor       # fp32 [n_slots][H_v][d_v][d_k]
+    conv_state: torch.Tensor  # fp32 [n_slots][R][C]
+    conv_pos: torch.Tensor    # int32 [n_slots], units of 1/65536 token
+
+    @staticmethod
+    def zeros(geom: Geometry, device="cuda") -> "SlotPool":
+        C, R = geom.conv_channels, max(geom.conv_ring, 1)
+        return SlotPool(
+            torch.zeros(geom.n_slots, geom.n_v_heads, geom.d_v, geom.d_k, dtype=torch.float32, device=device),
+            torch.zeros(geom.n_slots, R, C, dtype=torch.float32, device=device),
+            torch.zeros(geom.n_slots, dtype=torch.int32, device=device))
+
+
+def _check_pool(geom: Geometry, pool: SlotPool):
+    _need(pool.state, "state", (geom.n_slots, geom.n_v_heads, geom.d_v, geom.d_k), torch.float32)
+    if geom.conv_width > 0:
+        _need(pool.conv_state, "conv_state", (geom.n_slots, geom.conv_ring, geom.conv_channels), torch.float32)
+        _need(pool.conv_pos, "conv_pos", (geom.n_slots,), torch.int32)
+
+
+# --------------------------------------------------------------------------
+# the five entry points
+# --------------------------------------------------------------------------
+
+def conv_state_step(geom: Geometry, pool: SlotPool, x, conv_w, slot, y, dev_err=None, stream=None):
+    """gdn_conv_state_step: y = SiLU(causal conv) for all channels; append x to the ring."""
+    B = slot.shape[0]
+    C = geom.conv_channels
+    _check_pool(geom, pool)
+    _need(x, "x", (B, C), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32)
+    _need(slot, "slot", (B,), torch.int32)
+    _need(y, "y", (B, C), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_conv_state_step(ctypes.byref(g), _ptr(pool.conv_state), _ptr(pool.conv_pos), _ptr(x),
+                                     _ptr(conv_w), _ptr(slot), B, _ptr(y), _ptr(dev_err), _stream(stream)))
+
+
+def decode_step(geom: Geometry, pool: SlotPool, x, a, b, conv_w, slot, o, dev_err=None, stream=None):
+    """gdn_decode_step: one fused token per batch row; state updated in place."""
+    B = slot.shape[0]
+    C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
+    _check_pool(geom, pool)
+    _need(x, "x", (B, C), geom.dtype)
+    _need(a, "a", (B, Hv), geom.dtype)
+    _need(b, "b", (B, Hv), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
+    _need(slot, "slot", (B,), torch.int32)
+    _need(o, "o", (B, Hv, dv), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_decode_step(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state), _ptr(pool.conv_pos),
+                                 _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(slot), B, _ptr(o),
+                                 _ptr(dev_err), _stream(stream)))
+
+
+def verify_k(geom: Geometry, pool: SlotPool, x, a, b, conv_w, slot, snap, o, dev_err=None, stream=None):
+    """gdn_verify_k: k drafts per batch row, snapshot after each; committed state untouched."""
+    B, k = x.shape[0], x.shape[1]
+    C, Hv, dv, dk = geom.conv_channels, geom.n_v_heads, geom.d_v, geom.d_k
+    _check_pool(geom, pool)
+    _need(x, "x", (B, k, C), geom.dtype)
+    _need(a, "a", (B, k, Hv), geom.dtype)
+    _need(b, "b", (B, k, Hv), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
+    _need(slot, "slot", (B,), torch.int32)
+    _need(snap, "snap", (B, k, Hv, dv, dk), torch.float32)
+    _need(o, "o", (B, k, Hv, dv), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_verify_k(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state), _ptr(pool.conv_pos),
+                              _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(slot), B, k, _ptr(snap), _ptr(o),
+                              _ptr(dev_err), _stream(stream)))
+
+
+def rollback(geom: Geometry, pool: SlotPool, snap, slot, accepted, dev_err=None, stream=None):
+    """gdn_rollback: commit accepted[i] drafts of batch row i (0 keeps the slot as it was)."""
+    B, k = snap.shape[0], snap.shape[1]
+    _check_pool(geom, pool)
+    _need(snap, "snap", (B, k, geom.n_v_heads, geom.d_v, geom.d_k), torch.float32)
+    _need(slot, "slot", (B,), torch.int32)
+    _need(accepted, "accepted", (B,), torch.int32)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_rollback(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_pos), _ptr(snap), _ptr(slot),
+                              _ptr(accepted), B, k, _ptr(dev_err), _stream(stream)))
+
+
+def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_seqs: int) -> int:
+    g = geom.c_struct()
+    return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(g), n_tokens, n_seqs))
+
+
+def alloc_prefill_workspace(geom: Geometry, n_tokens: int, n_seqs: int, device="cuda") -> torch.Tensor:
+    """A caller-owned workspace of the size gdn_prefill_workspace_bytes reports."""
+    n = prefill_workspace_bytes(geom, n_tokens, n_seqs)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens, slot, has_init, o,
+                    workspace, dev_err=None, stream=None):
+    """gdn_prefill_chunked: varlen chunked prefill; final states and histories go to the slots."""
+    N = x.shape[0]
+    S = slot.shape[0]
+    C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
+    _check_pool(geom, pool)
+    _need(x, "x", (N, C), geom.dtype)
+    _need(a, "a", (N, Hv), geom.dtype)
+    _need(b, "b", (N, Hv), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
+    _need(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32)
+    _need(slot, "slot", (S,), torch.int32)
+    _need(has_init, "has_init", (S,), torch.int32)
+    _need(o, "o", (N, Hv, dv), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous device tensor")
+    g = geom.c_struct()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill_chunked(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
+                                     _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w),
+                                     _ptr(cu_seqlens), _ptr(slot), _ptr(has_init), S, N, CHUNK,
+                                     _ptr(workspace), nbytes, _ptr(o), _ptr(dev_err), _stream(stream)))
+
+
+__all__ = [
+    "Geometry", "GdnGeometry", "GdnError", "SlotPool", "lib", "conv_state_step", "decode_step", "verify_k",
+    "rollback", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace", "POS_ONE", "CHUNK",
+    "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS",
+]

@@ -1,0 +1,365 @@
+// C ABI of the GDN library: argument validation and dispatch to the kernel
+// launchers.  Host code only; nothing here touches the GPU except the
+// launches themselves, which are asynchronous on the caller's stream.
+//
+// Every refusal names the argument, the value found and the value required
+// ("Chapter 6: engine startup and memory plan", section 6.2), and no error is
+// swallowed: a launch the runtime refuses is returned as GDN_ERR_LAUNCH with
+// the runtime's code ("Forge", entry of 27 August: the costliest defect of
+// the week was an error the scheduler dropped without a log line).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define GDN_NEED_PTR(p, name)                                                     \
+  do {                                                                            \
+    if (!(p)) return fail(GDN_ERR_NULL, "%s: NULL, required: a device pointer", name); \
+    if (!aligned16(p))                                                            \
+      return fail(GDN_ERR_ALIGN, "%s: address %p, required: 16-byte aligned", name, \
+                  static_cast<const void*>(p));                                  \
+  } while (0)
+
+#define GDN_NEED_PTR4(p, name)                                                    \
+  do {                                                                            \
+    if (!(p)) return fail(GDN_ERR_NULL, "%s: NULL, required: a device pointer", name); \
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0)                               \
+      return fail(GDN_ERR_ALIGN, "%s: address %p, required: 4-byte aligned", name, \
+                  static_cast<const void*>(p));                                  \
+  } while (0)
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Largest number of workgroups one decode call puts on one slot; the
+// position shares must each be at least one unit.
+int step_wgs_per_slot(const gdn_geometry& g) {
+  const int D = g.d_k;
+  const int lpr = D / 4, rpw = 64 / lpr, np = D >= 64 ? 4 : (D >= 32 ? 2 : 1);
+  const int rows_wave = rpw * np;
+  const int nw = (D / rows_wave) < 4 ? (D / rows_wave) : 4;
+  return g.n_v_heads * (D / (nw * rows_wave));
+}
+
+gdn_status check_geometry(const gdn_geometry* g) {
+  if (!g) return fail(GDN_ERR_NULL, "geometry: NULL, required: a gdn_geometry");
+  if (g->n_k_heads < 1) return fail(GDN_ERR_GEOMETRY, "n_k_heads: %d, required: >= 1", g->n_k_heads);
+  if (g->n_v_heads < 1) return fail(GDN_ERR_GEOMETRY, "n_v_heads: %d, required: >= 1", g->n_v_heads);
+  if (g->n_v_heads % g->n_k_heads != 0)
+    return fail(GDN_ERR_GEOMETRY, "n_v_heads: %d, required: a multiple of n_k_heads = %d", g->n_v_heads,
+                g->n_k_heads);
+  if (g->d_k < 1 || g->d_v < 1)
+    return fail(GDN_ERR_GEOMETRY, "d_k, d_v: %d, %d, required: >= 1", g->d_k, g->d_v);
+  if (g->conv_width < 0 || g->conv_width > 4)
+    return fail(GDN_ERR_GEOMETRY, "conv_width: %d, required: 0..4", g->conv_width);
+  const long long chan = 2LL * g->n_k_heads * g->d_k + 1LL * g->n_v_heads * g->d_v;
+  if (g->conv_channels != chan)
+    return fail(GDN_ERR_GEOMETRY, "conv_channels: %d, required: 2*n_k_heads*d_k + n_v_heads*d_v = %lld",
+                g->conv_channels, chan);
+  if (g->max_draft < 1 || g->max_draft > 16)
+    return fail(GDN_ERR_GEOMETRY, "max_draft: %d, required: 1..16", g->max_draft);
+  if (g->conv_width > 0) {
+    const int need = g->conv_width - 1 + g->max_draft;
+    if (!pow2(g->conv_ring) || g->conv_ring < need)
+      return fail(GDN_ERR_GEOMETRY,
+                  "conv_ring: %d, required: a power of two >= conv_width-1+max_draft = %d", g->conv_ring,
+                  need);
+    if (g->conv_ring > (1 << 16))
+      return fail(GDN_ERR_GEOMETRY, "conv_ring: %d, required: <= 65536", g->conv_ring);
+  }
+  if (g->n_slots < 1) return fail(GDN_ERR_GEOMETRY, "n_slots: %d, required: >= 1", g->n_slots);
+  if (g->dtype_in != GDN_F32 && g->dtype_in != GDN_BF16)
+    return fail(GDN_ERR_GEOMETRY, "dtype_in: %d, required: GDN_F32 (0) or GDN_BF16 (1)", g->dtype_in);
+  if (g->dtype_out != g->dtype_in)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype_out: %d, required: equal to dtype_in = %d", g->dtype_out,
+                g->dtype_in);
+  if (g->flags & ~GDN_FLAG_L2NORM_QK)
+    return fail(GDN_ERR_GEOMETRY, "flags: 0x%x, required: a subset of GDN_FLAG_L2NORM_QK (0x1)", g->flags);
+  if (!std::isfinite(g->q_scale)) return fail(GDN_ERR_GEOMETRY, "q_scale: %g, required: finite", g->q_scale);
+  if (!std::isfinite(g->l2_eps) || g->l2_eps < 0.f)
+    return fail(GDN_ERR_GEOMETRY, "l2_eps: %g, required: finite and >= 0", g->l2_eps);
+  if (g->d_k != g->d_v)
+    return fail(GDN_ERR_UNSUPPORTED, "d_v: %d, required in this build: equal to d_k = %d", g->d_v, g->d_k);
+  if (g->d_k != 16 && g->d_k != 32 && g->d_k != 64 && g->d_k != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d, required in this build: 16, 32, 64 or 128", g->d_k);
+  if (g->n_v_heads / g->n_k_heads > 8)
+    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads/n_k_heads: %d, required in this build: <= 8",
+                g->n_v_heads / g->n_k_heads);
+  if (step_wgs_per_slot(*g) > (1 << 16))
+    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads: %d, required in this build: at most %d workgroups per slot",
+                g->n_v_heads, 1 << 16);
+  return ok();
+}
+
+gdn::StepArgs step_args(const gdn_geometry* g) {
+  gdn::StepArgs a{};
+  a.Hk = g->n_k_heads;
+  a.Hv = g->n_v_heads;
+  a.D = g->d_k;
+  a.C = g->conv_channels;
+  a.W = g->conv_width;
+  a.R = g->conv_ring;
+  a.n_slots = g->n_slots;
+  a.flags = g->flags;
+  a.q_scale = g->q_scale;
+  a.l2_eps = g->l2_eps;
+  return a;
+}
+
+gdn_status launched(int err, const char* what) {
+  if (err != 0) return fail(GDN_ERR_LAUNCH, "%s: HIP launch failed with error %d", what, err);
+  return ok();
+}
+
+gdn_status check_batch(int32_t batch, const gdn_geometry* g) {
+  if (batch < 1 || batch > g->n_slots)
+    return fail(GDN_ERR_RANGE, "batch: %d, required: 1..n_slots = %d", batch, g->n_slots);
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN";
+    case GDN_ERR_GEOMETRY: return "GDN_ERR_GEOMETRY";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_RANGE: return "GDN_ERR_RANGE";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+const char* gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
+
+gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len) {
+  const gdn_status s = check_geometry(g);
+  if (msg && msg_len) {
+    std::strncpy(msg, g_last_error.c_str(), msg_len - 1);
+    msg[msg_len - 1] = '\0';
+  }
+  return s;
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_geometry* g, int32_t n_tokens, int32_t n_seqs) {
+  if (check_geometry(g) != GDN_OK || n_tokens < 0 || n_seqs < 1) return 0;
+  const int maxc = gdn::prefill_max_chunks(n_tokens, n_seqs);
+  return gdn::prefill_layout(g->n_k_heads, g->n_v_heads, g->d_k, g->dtype_in == GDN_BF16, maxc, n_seqs).total;
+}
+
+gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t* conv_pos, const void* x,
+                               const float* conv_w, const int32_t* slot, int32_t batch, void* y,
+                               int32_t* dev_err, void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if (g->conv_width < 1)
+    return fail(GDN_ERR_GEOMETRY, "conv_width: %d, required: >= 1 for gdn_conv_state_step", g->conv_width);
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  GDN_NEED_PTR(conv_state, "conv_state");
+  GDN_NEED_PTR4(conv_pos, "conv_pos");
+  GDN_NEED_PTR(x, "x");
+  GDN_NEED_PTR(conv_w, "conv_w");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR(y, "y");
+  gdn::StepArgs a = step_args(g);
+  a.conv_state = conv_state;
+  a.conv_pos = conv_pos;
+  a.x = x;
+  a.conv_w = conv_w;
+  a.slot = slot;
+  a.o = y;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = 1;
+  return launched(gdn::launch_conv_step(a, g->dtype_in == GDN_BF16, stream), "gdn_conv_state_step");
+}
+
+gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                           const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                           const int32_t* slot, int32_t batch, void* o, int32_t* dev_err, void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  GDN_NEED_PTR(state, "state");
+  if (g->conv_width > 0) {
+    GDN_NEED_PTR(conv_state, "conv_state");
+    GDN_NEED_PTR4(conv_pos, "conv_pos");
+    GDN_NEED_PTR(conv_w, "conv_w");
+  }
+  GDN_NEED_PTR(x, "x");
+  GDN_NEED_PTR(a_in, "a");
+  GDN_NEED_PTR(b_in, "b");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR(o, "o");
+  gdn::StepArgs a = step_args(g);
+  a.state = state;
+  a.conv_state = conv_state;
+  a.conv_pos = conv_pos;
+  a.x = x;
+  a.a = a_in;
+  a.b = b_in;
+  a.conv_w = conv_w;
+  a.slot = slot;
+  a.o = o;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = 1;
+  return launched(gdn::launch_decode(a, g->dtype_in == GDN_BF16, stream), "gdn_decode_step");
+}
+
+gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_state, const int32_t* conv_pos,
+                        const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                        const int32_t* slot, int32_t batch, int32_t k, float* snap, void* o, int32_t* dev_err,
+                        void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  if (k < 1 || k > g->max_draft)
+    return fail(GDN_ERR_RANGE, "k: %d, required: 1..max_draft = %d", k, g->max_draft);
+  GDN_NEED_PTR(state, "state");
+  if (g->conv_width > 0) {
+    GDN_NEED_PTR(conv_state, "conv_state");
+    GDN_NEED_PTR4(conv_pos, "conv_pos");
+    GDN_NEED_PTR(conv_w, "conv_w");
+  }
+  GDN_NEED_PTR(x, "x");
+  GDN_NEED_PTR(a_in, "a");
+  GDN_NEED_PTR(b_in, "b");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR(snap, "snap");
+  GDN_NEED_PTR(o, "o");
+  gdn::StepArgs a = step_args(g);
+  a.state = const_cast<float*>(state);  // read only in verify
+  a.conv_state = conv_state;
+  a.conv_pos = const_cast<int32_t*>(conv_pos);
+  a.x = x;
+  a.a = a_in;
+  a.b = b_in;
+  a.conv_w = conv_w;
+  a.slot = slot;
+  a.o = o;
+  a.snap = snap;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = k;
+  return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k");
+}
+
+gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos, const float* snap,
+                        const int32_t* slot, const int32_t* accepted, int32_t batch, int32_t k, int32_t* dev_err,
+                        void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  if (k < 1 || k > g->max_draft)
+    return fail(GDN_ERR_RANGE, "k: %d, required: 1..max_draft = %d", k, g->max_draft);
+  GDN_NEED_PTR(state, "state");
+  if (g->conv_width > 0) GDN_NEED_PTR4(conv_pos, "conv_pos");
+  GDN_NEED_PTR(snap, "snap");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR4(accepted, "accepted");
+  gdn::StepArgs a = step_args(g);
+  a.state = state;
+  a.conv_pos = conv_pos;
+  a.snap = const_cast<float*>(snap);
+  a.slot = slot;
+  a.accepted = accepted;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = k;
+  return launched(gdn::launch_rollback(a, stream), "gdn_rollback");
+}
+
+gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                               const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                               const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
+                               int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, void* o, int32_t* dev_err, void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if (chunk != gdn::kChunk)
+    return fail(GDN_ERR_UNSUPPORTED, "chunk: %d, required in this build: %d", chunk, gdn::kChunk);
+  if (n_seqs < 1 || n_seqs > g->n_slots)
+    return fail(GDN_ERR_RANGE, "n_seqs: %d, required: 1..n_slots = %d", n_seqs, g->n_slots);
+  if (n_tokens < 0) return fail(GDN_ERR_RANGE, "n_tokens: %d, required: >= 0", n_tokens);
+  const size_t need = gdn_prefill_workspace_bytes(g, n_tokens, n_seqs);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace_bytes: %zu, required: >= %zu", workspace_bytes, need);
+  GDN_NEED_PTR(state, "state");
+  if (g->conv_width > 0) {
+    GDN_NEED_PTR(conv_state, "conv_state");
+    GDN_NEED_PTR4(conv_pos, "conv_pos");
+    GDN_NEED_PTR(conv_w, "conv_w");
+  }
+  if (n_tokens > 0) {
+    GDN_NEED_PTR(x, "x");
+    GDN_NEED_PTR(a_in, "a");
+    GDN_NEED_PTR(b_in, "b");
+    GDN_NEED_PTR(o, "o");
+  }
+  GDN_NEED_PTR4(cu_seqlens, "cu_seqlens");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR4(has_init, "has_init");
+  GDN_NEED_PTR(workspace, "workspace");
+  gdn::PrefillArgs a{};
+  a.state = state;
+  a.conv_state = conv_state;
+  a.conv_pos = conv_pos;
+  a.x = x;
+  a.a = a_in;
+  a.b = b_in;
+  a.conv_w = conv_w;
+  a.cu_seqlens = cu_seqlens;
+  a.slot = slot;
+  a.has_init = has_init;
+  a.o = o;
+  a.dev_err = dev_err;
+  a.workspace = workspace;
+  a.n_seqs = n_seqs;
+  a.n_tokens = n_tokens;
+  a.max_chunks = gdn::prefill_max_chunks(n_tokens, n_seqs);
+  a.Hk = g->n_k_heads;
+  a.Hv = g->n_v_heads;
+  a.D = g->d_k;
+  a.C = g->conv_channels;
+  a.W = g->conv_width;
+  a.R = g->conv_ring;
+  a.n_slots = g->n_slots;
+  a.flags = g->flags;
+  a.q_scale = g->q_scale;
+  a.l2_eps = g->l2_eps;
+  return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream), "gdn_prefill_chunked");
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device helpers shared by the GDN kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kWave = 64;
+constexpr int kPosShift = 16;  // conv_pos counts tokens in units of 1/65536
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 kept as its 16-bit pattern)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.  Written as a select, not a branch,
+// so that long unrolled store sequences stay straight-line code.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? nan : rne);
+}
+
+// Element access for the two input/output dtypes: BF16 = true reads bf16 bits.
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void* p, size_t i) {
+  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* p, size_t i, float v) {
+  if constexpr (BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  else static_cast<float*>(p)[i] = v;
+}
+
+// Four consecutive elements starting at element i (i multiple of 4).
+template <bool BF16>
+__device__ __forceinline__ float4 load_in4(const void* p, size_t i) {
+  if constexpr (BF16) {
+    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scalar laws: beta = sigmoid(b), g = log(alpha) = -softplus(a)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu_f(float y) { return y * sigmoid_f(y); }
+
+// ---------------------------------------------------------------------------
+// Reductions inside groups of N consecutive lanes (N a power of two <= 64),
+// always in the same butterfly order, so results are reproducible.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = N / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Device error word: the first code of a call wins.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void report_error(int32_t* dev_err, int32_t code) {
+  if (dev_err) atomicCAS(dev_err, 0, code);
+}
+
+// Ring row of token position p (R a power of two).
+__device__ __forceinline__ int ring_row(uint32_t p, int R) { return static_cast<int>(p & (R - 1)); }
+
+// Non-temporal 16-byte store (state and snapshots are streamed, not reused).
+__device__ __forceinline__ void store_nt4(float* p, f32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ f32x4_t load4(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+
+}  // namespace gdn

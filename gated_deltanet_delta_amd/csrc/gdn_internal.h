@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI layer (gdn_api.cpp) and the kernel
+// launchers (gdn_step.hip, gdn_prefill.hip).  Host code only.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Arguments of the per-token kernels (decode, verify, conv step, rollback).
+struct StepArgs {
+  float* state;          // decode: in/out; verify: in; rollback: out
+  float* conv_state;
+  int32_t* conv_pos;
+  const void* x;
+  const void* a;
+  const void* b;
+  const float* conv_w;
+  const int32_t* slot;
+  const int32_t* accepted;  // rollback only
+  void* o;                  // o, or y for the conv step
+  float* snap;              // verify: out; rollback: in
+  int32_t* dev_err;
+  int32_t batch, k;
+  int32_t Hk, Hv, D, C, W, R, n_slots;
+  uint32_t flags;
+  float q_scale, l2_eps;
+};
+
+struct PrefillArgs {
+  float* state;
+  float* conv_state;
+  int32_t* conv_pos;
+  const void* x;
+  const void* a;
+  const void* b;
+  const float* conv_w;
+  const int32_t* cu_seqlens;
+  const int32_t* slot;
+  const int32_t* has_init;
+  void* o;
+  int32_t* dev_err;
+  void* workspace;
+  int32_t n_seqs, n_tokens, max_chunks;
+  int32_t Hk, Hv, D, C, W, R, n_slots;
+  uint32_t flags;
+  float q_scale, l2_eps;
+};
+
+// Byte offsets of the prefill workspace regions.
+struct PrefillLayout {
+  size_t q, k, kt, v, t, p, g, beta, chunk_tab, seq_tab, counters, total;
+};
+PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int max_chunks, int n_seqs);
+int prefill_max_chunks(int n_tokens, int n_seqs);
+constexpr int kChunk = 64;
+
+// Launchers: return 0 on success, else the hipError_t value.
+int launch_decode(const StepArgs& a, bool bf16, void* stream);
+int launch_verify(const StepArgs& a, bool bf16, void* stream);
+int launch_conv_step(const StepArgs& a, bool bf16, void* stream);
+int launch_rollback(const StepArgs& a, void* stream);
+int launch_prefill(const PrefillArgs& a, bool bf16, void* stream);
+
+}  // namespace gdn

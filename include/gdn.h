@@ -1,0 +1,228 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet layer library for AMD MI355X (gfx950).
+ *
+ * The layer (Gated DeltaNet, arXiv:2412.06464; described in words in
+ * "Hybrid transformers under load: where Gated DeltaNet loses to full
+ * attention", section 3) keeps a fixed-size fp32 state S (d_v x d_k) per
+ * v-head and, for every token,
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = q_scale * S_t q_t,
+ *
+ * with alpha_t = exp(-softplus(a_t)) and beta_t = sigmoid(b_t) from the raw
+ * gate inputs a, b, and q, k, v taken from the projected input x through a
+ * causal depthwise conv of width W, SiLU, and an L2 normalisation of q and k
+ * (x * (sum x^2 + l2_eps)^-1/2 per k-head).  The conv input channels are
+ * ordered q | k | v, each head-major; v-head h reads k-head h / (H_v / H_k).
+ *
+ * Three paths share one slot pool: a per-token decode step, a chunked
+ * (WY/UT-transform) prefill over variable-length sequences, and a k-draft
+ * speculative verify that writes a state snapshot after every draft so that
+ * rollback is a copy ("Forge: how I wrote my own inference engine and beat
+ * llama.cpp", entry of 27 August).
+ *
+ * Conventions for every call below
+ * --------------------------------
+ *  - Pointers are DEVICE pointers unless stated otherwise; every buffer is
+ *    owned by the caller.  The library never allocates, frees or synchronises
+ *    on these calls: work is enqueued on `stream` (a hipStream_t, NULL = the
+ *    default stream) and the call returns ("Chapter 6: engine startup and
+ *    memory plan", section 6.10: the token path allocates nothing).
+ *  - Problems the host can see (bad geometry, null or misaligned pointers,
+ *    sizes out of range, small workspace) return a nonzero gdn_status BEFORE
+ *    anything is launched; gdn_last_error() then names the argument, the value
+ *    found and the value required (same book, section 6.2: a mismatch is
+ *    reported with the name, the shape found and the shape required).
+ *  - Problems only the device can see (a slot id out of [0, n_slots), an
+ *    accepted length out of [0, k], cu_seqlens that are not a valid partition)
+ *    are written to *dev_err (if dev_err is not NULL) as the FIRST error code
+ *    of the call (later ones do not overwrite it) and the affected row is
+ *    skipped: nothing is clamped, nothing is written out of range.
+ *  - Buffers read or written by a call must not alias each other (x, a, b,
+ *    o, snap, workspace vs state and conv_state).  Slot ids within one call
+ *    must be distinct; duplicates give undefined results.
+ *  - Every pointer to float data and every x / o / snap / workspace pointer
+ *    must be 16-byte aligned.
+ *  - Calls on one stream are ordered; calls that overlap in time on the same
+ *    slots race.
+ *
+ * Layouts (row-major, last index fastest)
+ * ---------------------------------------
+ *  state      fp32  [n_slots][H_v][d_v][d_k]   slot pool of recurrent states
+ *  conv_state fp32  [n_slots][R][C]            conv ring of past inputs x
+ *  conv_pos   int32 [n_slots]                  ring position, in units of
+ *                                              1/GDN_POS_ONE token (below)
+ *  conv_w     fp32  [C][W]                     tap W-1 multiplies the current token
+ *  x          dtype_in  [rows][C]              projected input, q | k | v
+ *  a, b       dtype_in  [rows][H_v]            raw gate inputs
+ *  o          dtype_out [rows][H_v][d_v]
+ *
+ * The conv ring.  Row (p mod R) of a slot's ring holds the input x of the
+ * slot's token number p; the conv window of the next token reads rows
+ * p-W+1 .. p-1 (mod R) for the current position p.  conv_pos keeps p scaled
+ * by GDN_POS_ONE (65536) so that the many workgroups of one call can each add
+ * a fraction of one token without a second counter: readers take
+ * p = (uint32_t)conv_pos >> 16.  The ring must hold R >= W-1+max_draft rows
+ * (R a power of two) so verify can write its drafts ahead of the committed
+ * history without overwriting it.  Zero-initialising a slot's ring and
+ * conv_pos gives an all-zero history.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_POS_ONE 65536
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,          /* a required pointer is NULL */
+  GDN_ERR_ALIGN = 2,         /* a pointer is not 16-byte aligned */
+  GDN_ERR_GEOMETRY = 3,      /* inconsistent gdn_geometry */
+  GDN_ERR_UNSUPPORTED = 4,   /* a valid geometry this build has no kernels for */
+  GDN_ERR_RANGE = 5,         /* a size argument out of range (batch, k, n_tokens...) */
+  GDN_ERR_WORKSPACE = 6,     /* workspace smaller than gdn_prefill_workspace_bytes() */
+  GDN_ERR_LAUNCH = 7         /* the HIP runtime refused a launch */
+} gdn_status;
+
+/* Device-side error codes written to *dev_err (first one wins). */
+#define GDN_DEV_OK 0
+#define GDN_DEV_BAD_SLOT 1       /* slot id outside [0, n_slots) */
+#define GDN_DEV_BAD_ACCEPTED 2   /* accepted length outside [0, k] */
+#define GDN_DEV_BAD_SEQLENS 3    /* cu_seqlens[0] != 0, decreasing, or last != n_tokens */
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+#define GDN_FLAG_L2NORM_QK 1u    /* L2-normalise q and k after the front end */
+
+/*
+ * Geometry of one layer.  Every field is a number some kernel depends on
+ * ("Chapter 6: engine startup and memory plan", section 6.2, ModelGeometry:
+ * ssm_state_size = 128, ssm_k_heads = 16, ssm_v_heads = 48, ssm_d_conv = 4,
+ * ssm_conv_channels = 10240 = 2*128*16 + 128*48).
+ */
+typedef struct gdn_geometry {
+  int32_t n_k_heads;      /* H_k */
+  int32_t n_v_heads;      /* H_v, a multiple of H_k */
+  int32_t d_k;            /* state columns (ssm_state_size) */
+  int32_t d_v;            /* state rows; this build requires d_v == d_k in {16,32,64,128} */
+  int32_t conv_width;     /* W in {0,2,3,4}; 0 = no conv and no SiLU: x holds q | k | v */
+  int32_t conv_channels;  /* C, must equal 2*H_k*d_k + H_v*d_v */
+  int32_t conv_ring;      /* R, power of two >= W-1+max_draft (ignored when W = 0) */
+  int32_t max_draft;      /* largest k accepted by gdn_verify_k (1..16) */
+  int32_t n_slots;        /* pool size */
+  int32_t dtype_in;       /* gdn_dtype of x, a, b */
+  int32_t dtype_out;      /* gdn_dtype of o and of gdn_conv_state_step's y; == dtype_in */
+  uint32_t flags;         /* GDN_FLAG_* */
+  float q_scale;          /* output scale; 1.0 computes o = S q as written */
+  float l2_eps;           /* epsilon under the square root of the L2 norm (1e-6) */
+} gdn_geometry;
+
+/* Human-readable name of a status code (static storage). */
+const char* gdn_status_string(gdn_status s);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Library version string (static storage). */
+const char* gdn_version(void);
+
+/*
+ * Validate a geometry without touching the GPU.  Returns GDN_OK, or an error
+ * with a message (also copied into msg when msg != NULL, NUL-terminated,
+ * truncated to msg_len) naming the field, the value found and the value
+ * required.  GDN_ERR_UNSUPPORTED means consistent but not built here.
+ */
+gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len);
+
+/*
+ * Workspace bytes gdn_prefill_chunked needs for n_tokens tokens in n_seqs
+ * sequences with 64-token chunks (0 when the geometry is invalid).  Host only.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_geometry* g, int32_t n_tokens, int32_t n_seqs);
+
+/*
+ * One token of the conv ring alone: for each batch row i with slot s = slot[i],
+ *   y[i][c] = SiLU(sum_j conv_w[c][j] * window_j[c])   (window: W-1 ring rows, then x[i])
+ * then x[i] is appended to the slot's ring and conv_pos[s] advances by one token.
+ * (Conv width 4 and channel count: "Chapter 6", section 6.2; the conv part of
+ * the per-layer state: "Hybrid transformers under load", section 4.1.)
+ *   x [batch][C] dtype_in, y [batch][C] dtype_out, slot [batch] int32 (device).
+ * Requires W > 0.  1 <= batch <= n_slots.
+ */
+gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t* conv_pos,
+                               const void* x, const float* conv_w, const int32_t* slot,
+                               int32_t batch, void* y, int32_t* dev_err, void* stream);
+
+/*
+ * One decode token per batch row, fused: conv ring + SiLU, L2 norm of q and k,
+ * gates, the delta-rule update of the slot's state in place, and the output.
+ * Each fp32 state row is read once and written once.
+ *   x [batch][C], a, b [batch][H_v] (dtype_in); o [batch][H_v][d_v] (dtype_out);
+ *   slot [batch] int32 (device).  Advances conv_pos of each slot by one token.
+ *   1 <= batch <= n_slots.
+ */
+gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_state,
+                           int32_t* conv_pos, const void* x, const void* a, const void* b,
+                           const float* conv_w, const int32_t* slot, int32_t batch, void* o,
+                           int32_t* dev_err, void* stream);
+
+/*
+ * Chunked prefill of n_seqs sequences packed along the token axis
+ * (cu_seqlens [n_seqs+1] int32, device: sequence s is tokens
+ * [cu_seqlens[s], cu_seqlens[s+1])).  Sequence s starts from slot[s]'s state
+ * and conv history when has_init[s] != 0, from zeros otherwise; its final
+ * state and conv history are written back to slot[s] and conv_pos[slot[s]]
+ * ends n_s tokens after the start position (0 when has_init[s] == 0).
+ * Chunks of `chunk` = 64 tokens never straddle two sequences; the last chunk
+ * of a sequence may be partial.  Results equal the token-by-token rule up to
+ * rounding (the chunked form is an exact reorganisation).
+ *   x [n_tokens][C], a, b [n_tokens][H_v] (dtype_in); o [n_tokens][H_v][d_v];
+ *   slot, has_init [n_seqs] int32 (device).
+ *   workspace: device, >= gdn_prefill_workspace_bytes(g, n_tokens, n_seqs).
+ *   1 <= n_seqs <= n_slots, 0 <= n_tokens.
+ */
+gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_state,
+                               int32_t* conv_pos, const void* x, const void* a, const void* b,
+                               const float* conv_w, const int32_t* cu_seqlens,
+                               const int32_t* slot, const int32_t* has_init, int32_t n_seqs,
+                               int32_t n_tokens, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, void* o, int32_t* dev_err, void* stream);
+
+/*
+ * Speculative verify of k draft tokens per batch row ("Forge", 27 August:
+ * the DeltaNet state walks the draft rows in order, with a snapshot of the
+ * state after every row).  For draft j = 0..k-1 it computes the same per-token
+ * math as gdn_decode_step, bit for bit, and writes
+ *   snap [batch][k][H_v][d_v][d_k] fp32 = state after draft j,
+ *   o    [batch][k][H_v][d_v]      dtype_out.
+ * The committed state and conv_pos are NOT modified; the drafts' inputs are
+ * written into ring rows p .. p+k-1 ahead of the committed history.
+ *   x [batch][k][C], a, b [batch][k][H_v] (dtype_in).  1 <= k <= max_draft.
+ */
+gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_state,
+                        const int32_t* conv_pos, const void* x, const void* a, const void* b,
+                        const float* conv_w, const int32_t* slot, int32_t batch, int32_t k,
+                        float* snap, void* o, int32_t* dev_err, void* stream);
+
+/*
+ * Commit accepted drafts after gdn_verify_k (same slot, batch, k and snap):
+ * for each batch row with n = accepted[i] (device int32 [batch], 0..k):
+ * if n >= 1 the slot's state becomes a bitwise copy of snap[i][n-1] and
+ * conv_pos advances n tokens; n = 0 leaves the slot unchanged.
+ */
+gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos,
+                        const float* snap, const int32_t* slot, const int32_t* accepted,
+                        int32_t batch, int32_t k, int32_t* dev_err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,176 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/gdn.h declares, validates geometries and refuses bad
+arguments with a message naming the argument, the value and the requirement
+-- before anything would be launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_delta_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from gated_deltanet_delta_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_conv_state_step", "gdn_decode_step", "gdn_prefill_chunked", "gdn_verify_k", "gdn_rollback"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(gdn):
+    L = gdn.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def _geom(gdn, **kw):
+    return gdn.Geometry(**kw).c_struct()
+
+
+def _check(gdn, g):
+    buf = ctypes.create_string_buffer(256)
+    st = gdn.lib().gdn_check_geometry(ctypes.byref(g), buf, 256)
+    return st, buf.value.decode()
+
+
+def test_valid_geometries(gdn):
+    assert _check(gdn, _geom(gdn))[0] == 0
+    tiny = _geom(gdn, n_k_heads=1, n_v_heads=1, d_k=16, d_v=16, conv_width=0, n_slots=1)
+    tiny.dtype_in = tiny.dtype_out = gdn.GDN_F32
+    assert _check(gdn, tiny)[0] == 0
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("n_v_heads", 47, 3, "n_v_heads: 47, required: a multiple of n_k_heads = 16"),
+    ("conv_channels", 10000, 3, "conv_channels: 10000, required: 2*n_k_heads*d_k + n_v_heads*d_v = 10240"),
+    ("conv_ring", 6, 3, "conv_ring: 6, required: a power of two >= conv_width-1+max_draft = 7"),
+    ("conv_ring", 4, 3, "conv_ring: 4"),
+    ("conv_width", 5, 3, "conv_width: 5, required: 0..4"),
+    ("max_draft", 0, 3, "max_draft: 0"),
+    ("n_slots", 0, 3, "n_slots: 0"),
+    ("dtype_in", 7, 3, "dtype_in: 7"),
+    ("flags", 6, 3, "flags: 0x6"),
+])
+def test_geometry_refusals_name_found_and_required(gdn, field, value, status, needle):
+    g = _geom(gdn)
+    setattr(g, field, value)
+    st, msg = _check(gdn, g)
+    assert st == status and needle in msg, msg
+
+
+def test_unsupported_sizes_are_refused_not_emulated(gdn):
+    g = _geom(gdn, d_k=96, d_v=96)
+    st, msg = _check(gdn, g)
+    assert st == 4 and "d_k: 96" in msg
+    g = _geom(gdn, d_k=128, d_v=64)
+    st, msg = _check(gdn, g)
+    assert st == 4 and "d_v: 64" in msg
+    g = _geom(gdn, n_k_heads=1, n_v_heads=16)
+    st, msg = _check(gdn, g)
+    assert st == 4 and "n_v_heads/n_k_heads: 16" in msg
+
+
+def test_workspace_size(gdn):
+    g = _geom(gdn)
+    L = gdn.lib()
+    n1 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 8192, 1)
+    n2 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 16384, 1)
+    assert n1 > 0 and n2 > n1
+    # per 64-token chunk: q, k, k^T (16 heads) + v, T, P (48 heads) in bf16 + fp32 gates
+    per_chunk = 3 * 16 * 64 * 128 * 2 + 48 * 64 * 128 * 2 + 2 * 48 * 64 * 64 * 2 + 2 * 48 * 64 * 4
+    assert abs(n1 - 129 * per_chunk) < 64 * 1024
+    bad = _geom(gdn, n_v_heads=47)
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(bad), 8192, 1) == 0
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails validation first
+
+
+def _p(v=FAKE):
+    return ctypes.c_void_p(v)
+
+
+def test_decode_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn)
+    args = lambda **o: [ctypes.byref(g)] + [o.get(n, _p()) for n in  # noqa: E731
+                                            ("state", "conv_state", "conv_pos", "x", "a", "b", "conv_w", "slot")] \
+        + [o.get("batch", 4), o.get("o", _p()), None, None]
+    assert L.gdn_decode_step(*args(batch=0)) == 5
+    assert "batch: 0, required: 1..n_slots = 8" in L.gdn_last_error().decode()
+    assert L.gdn_decode_step(*args(batch=9)) == 5
+    assert L.gdn_decode_step(*args(state=None)) == 1
+    assert "state: NULL" in L.gdn_last_error().decode()
+    assert L.gdn_decode_step(*args(x=_p(FAKE + 2))) == 2
+    assert "x: address" in L.gdn_last_error().decode() and "16-byte aligned" in L.gdn_last_error().decode()
+    assert L.gdn_decode_step(*args(conv_w=None)) == 1
+    g.n_v_heads = 47
+    assert L.gdn_decode_step(*args()) == 3
+
+
+def test_verify_and_rollback_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn)
+    va = lambda k: [ctypes.byref(g)] + [_p()] * 7 + [_p(), 4, k, _p(), _p(), None, None]  # noqa: E731
+    assert L.gdn_verify_k(*va(0)) == 5
+    assert L.gdn_verify_k(*va(5)) == 5
+    assert "k: 5, required: 1..max_draft = 4" in L.gdn_last_error().decode()
+    rb = [ctypes.byref(g), _p(), _p(), _p(), _p(), None, 4, 4, None, None]
+    assert L.gdn_rollback(*rb) == 1
+    assert "accepted: NULL" in L.gdn_last_error().decode()
+
+
+def test_prefill_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn)
+    need = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 8192, 1)
+
+    def call(chunk=64, ws=need, n_seqs=1, n_tokens=8192, cu=_p()):
+        return L.gdn_prefill_chunked(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), _p(), _p(), cu, _p(), _p(),
+                                     n_seqs, n_tokens, chunk, _p(), ws, _p(), None, None)
+    assert call(chunk=128) == 4
+    assert "chunk: 128, required in this build: 64" in L.gdn_last_error().decode()
+    assert call(ws=need - 1) == 6
+    assert f"required: >= {need}" in L.gdn_last_error().decode()
+    assert call(n_seqs=9) == 5
+    assert call(n_tokens=-1) == 5
+    assert call(cu=None) == 1
+
+
+def test_conv_step_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn, conv_width=0)
+    assert L.gdn_conv_state_step(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), 4, _p(), None, None) == 3
+    assert "conv_width: 0" in L.gdn_last_error().decode()
+
+
+def test_status_strings(gdn):
+    L = gdn.lib()
+    assert L.gdn_status_string(0) == b"GDN_OK"
+    assert L.gdn_status_string(6) == b"GDN_ERR_WORKSPACE"
+    assert b"gfx950" in L.gdn_version()
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import gated_deltanet_delta_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        m.lib()
