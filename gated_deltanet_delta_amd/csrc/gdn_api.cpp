@@ -102,6 +102,8 @@ gdn_status check_geometry(const gdn_geometry* g) {
   if (!std::isfinite(g->q_scale)) return fail(GDN_ERR_GEOMETRY, "q_scale: %g, required: finite", g->q_scale);
   if (!std::isfinite(g->l2_eps) || g->l2_eps < 0.f)
     return fail(GDN_ERR_GEOMETRY, "l2_eps: %g, required: finite and >= 0", g->l2_eps);
+  if (g->conv_width != 0 && g->conv_width != 4)
+    return fail(GDN_ERR_UNSUPPORTED, "conv_width: %d, required in this build: 0 or 4", g->conv_width);
   if (g->d_k != g->d_v)
     return fail(GDN_ERR_UNSUPPORTED, "d_v: %d, required in this build: equal to d_k = %d", g->d_v, g->d_k);
   if (g->d_k != 16 && g->d_k != 32 && g->d_k != 64 && g->d_k != 128)

@@ -19,13 +19,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest even; NaN stays NaN.  Written as a select, not a branch,
-// so that long unrolled store sequences stay straight-line code.
+// Round to nearest even (the hardware v_cvt_pk_bf16_f32 of gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t nan = (u >> 16) | 0x40u;
-  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? nan : rne);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Element access for the two input/output dtypes: BF16 = true reads bf16 bits.

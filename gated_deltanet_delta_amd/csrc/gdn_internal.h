@@ -49,9 +49,12 @@ struct PrefillArgs {
   float q_scale, l2_eps;
 };
 
-// Byte offsets of the prefill workspace regions.
+// Byte offsets and block sizes of the prefill workspace.
+//   kq:   per (chunk, k-head) block of packed K, Q and K^T operands (kq_bytes each)
+//   head: per (chunk, v-head) block of packed T, P, V and the gates (head_bytes each)
 struct PrefillLayout {
-  size_t q, k, kt, v, t, p, g, beta, chunk_tab, seq_tab, counters, total;
+  size_t kq, head, chunk_tab, seq_tab, counters, total;
+  size_t kq_bytes, head_bytes;
 };
 PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int max_chunks, int n_seqs);
 int prefill_max_chunks(int n_tokens, int n_seqs);

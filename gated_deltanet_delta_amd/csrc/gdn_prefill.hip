@@ -16,47 +16,98 @@
 //   plan:   one workgroup turns the device cu_seqlens into a chunk table
 //           (chunks restart at every sequence start; the last one may be
 //           partial) and validates slots and lengths -- no host sync;
-//   chunk:  one workgroup per (chunk, k-head): conv + SiLU + L2 norm of the
-//           chunk's q, k (and v of the k-head's v-heads), gates and their
-//           cumulative sums, A = K K^T and B = Q K^T on fp32 MFMA, then per
-//           v-head L, the inverse T by forward substitution (one lane per
-//           column, fp32), and P.  Everything goes to the workspace;
-//   state:  one workgroup per (sequence, v-head, block of d_v rows) walks the
-//           sequence's chunks in order with its fp32 state block resident in
-//           MFMA accumulators and computes U, O and the next state with bf16
-//           MFMA (fp32 MFMA for fp32 inputs).  It then writes the final state
-//           and the conv history back to the sequence's slot.
+//   chunk:  one workgroup per (chunk, k-head), all chunks in parallel: conv +
+//           SiLU + L2 norm of the chunk's q, k and v, gates and their
+//           cumulative sums, K K^T and Q K^T on MFMA, then per v-head L, the
+//           inverse T and P.  Every matrix the next kernel multiplies is
+//           written pre-packed in MFMA operand order (below), V already
+//           scaled by beta, and the per-token gate factors precomputed;
+//   chain:  one wave per (sequence, v-head, 16 rows of d_v) walks the
+//           sequence's chunks in order.  It keeps its 16 x d_k slice of the
+//           state, transposed, in MFMA accumulators and never leaves
+//           registers: every product's result feeds the next product as its
+//           B operand directly (the contraction order inside an MFMA is a
+//           free permutation, so the A operand is packed in the permuted
+//           order that matches the accumulator layout).  The waves of a
+//           workgroup share the chunk's packed operands, staged into LDS
+//           with direct global->LDS loads one chunk ahead.
+//
+// Packed operand tiles.  A 16 x SK sub-matrix (rows r, contraction index k;
+// SK = 32 for the bf16 MFMA 16x16x32, 16 for four fp32 MFMA 16x16x4) is
+// stored as 64 lanes x 16 bytes.  Lane (g = k%16 / 4) * 16 + r holds, in
+// element e = (k / 16) * 4 + k % 4, the value at (r, k).  A 16x16
+// accumulator tile holds rows 4g..4g+3 of column l%16 in lane l, so the
+// accumulators of tiles (2s, 2s+1) (bf16) or tile s (fp32) form exactly the
+// B operand that pairs with packed tile column s.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kC = kChunk;   // 64 tokens per chunk
-constexpr int kMaxGroup = 8; // v-heads per k-head supported by the chunk kernel
+constexpr int kC = kChunk;    // 64 tokens per chunk
+constexpr int kMaxGroup = 8;  // v-heads per k-head
+constexpr int kLd = kC + 1;   // row stride of 64x64 fp32 matrices in LDS
+constexpr int kTileBytes = 1024;
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+template <bool BF16>
+struct Pk {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  static constexpr int SK = BF16 ? 32 : 16;         // contraction length of one packed tile
+  static constexpr int EPL = BF16 ? 8 : 4;          // elements per lane (16 bytes)
+  static constexpr int VC_BYTES = 256 * sizeof(E);  // one 16x16 tile in accumulator layout
+};
+
+template <int D, bool BF16>
+struct Geo {
+  using P = Pk<BF16>;
+  static constexpr int KSD = (D + P::SK - 1) / P::SK;  // packed tiles along d
+  static constexpr int KSC = kC / P::SK;               // packed tiles along the chunk
+  static constexpr int NT = D / 16;                    // 16-row tiles along d
+  static constexpr int KA = 0;                         // K  as A (rows tok, k = d):   4 x KSD
+  static constexpr int QA = 4 * KSD;                   // Q  as A:                     4 x KSD
+  static constexpr int KTA = 8 * KSD;                  // K^T as A (rows d, k = tok): NT x KSC
+  static constexpr int KQ_TILES = 8 * KSD + NT * KSC;
+  static constexpr int TA = 0;                         // T as A (rows r, k = j):      4 x KSC
+  static constexpr int PA = 4 * KSC;                   // P as A:                      4 x KSC
+  static constexpr size_t VC_OFF = 8 * KSC * kTileBytes;            // V, accumulator layout [NT][4]
+  // per-token factors: e^G, beta e^G, e^{G_last - G}, then e^{G_last} (4 x 64 floats)
+  static constexpr size_t GATE_OFF = VC_OFF + NT * 4 * P::VC_BYTES;
+  static constexpr size_t GATE_BYTES = 4 * kC * 4;
+  static constexpr size_t KQ_BYTES = KQ_TILES * kTileBytes;
+  static constexpr size_t HEAD_BYTES = GATE_OFF + GATE_BYTES;
+};
+
 int prefill_max_chunks(int n_tokens, int n_seqs) { return (n_tokens + kC - 1) / kC + n_seqs; }
 
-PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int maxc, int S) {
-  const size_t es = bf16 ? 2 : 4;
+template <int D, bool BF16>
+static PrefillLayout layout_t(int Hk, int Hv, int maxc, int S) {
+  using Gm = Geo<D, BF16>;
   PrefillLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   const size_t mc = static_cast<size_t>(maxc);
-  L.q = take(mc * Hk * kC * D * es);
-  L.k = take(mc * Hk * kC * D * es);
-  L.kt = take(mc * Hk * D * kC * es);
-  L.v = take(mc * Hv * kC * D * es);
-  L.t = take(mc * Hv * kC * kC * es);
-  L.p = take(mc * Hv * kC * kC * es);
-  L.g = take(mc * Hv * kC * 4);
-  L.beta = take(mc * Hv * kC * 4);
+  L.kq_bytes = Gm::KQ_BYTES;
+  L.head_bytes = Gm::HEAD_BYTES;
+  L.kq = take(mc * Hk * Gm::KQ_BYTES);
+  L.head = take(mc * Hv * Gm::HEAD_BYTES);
   L.chunk_tab = take(mc * 4 * 4);
   L.seq_tab = take(static_cast<size_t>(S) * 8 * 4);
   L.counters = take(256);
   L.total = off;
   return L;
+}
+
+PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int maxc, int S) {
+  switch (D) {
+    case 16: return bf16 ? layout_t<16, true>(Hk, Hv, maxc, S) : layout_t<16, false>(Hk, Hv, maxc, S);
+    case 32: return bf16 ? layout_t<32, true>(Hk, Hv, maxc, S) : layout_t<32, false>(Hk, Hv, maxc, S);
+    case 64: return bf16 ? layout_t<64, true>(Hk, Hv, maxc, S) : layout_t<64, false>(Hk, Hv, maxc, S);
+    default: return bf16 ? layout_t<128, true>(Hk, Hv, maxc, S) : layout_t<128, false>(Hk, Hv, maxc, S);
+  }
 }
 
 // Sequence table entry (int32 x 8).
@@ -66,6 +117,14 @@ enum { SQF_VALID = 1, SQF_INIT = 2 };
 template <typename T>
 __device__ __forceinline__ T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Workgroup barrier that orders LDS traffic only: global loads issued before
+// it stay in flight (a full __syncthreads would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------------------
@@ -98,7 +157,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
       e[SQ_START] = st;
       e[SQ_LEN] = len;
       e[SQ_PAD] = 0;
-      total += nc > 0 ? nc : 0;
+      total += nc;
     }
     if (!ok) {
       report_error(A.dev_err, bad_code);
@@ -112,12 +171,11 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
   __syncthreads();
   const int total = s_total;
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
-    int lo = 0, hi = A.n_seqs - 1;  // last s with first <= c
+    int lo = 0, hi = A.n_seqs - 1;  // last s with first <= c holds c
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (stab[8 * mid + SQ_FIRST] <= c) lo = mid; else hi = mid - 1;
     }
-    // sequences after the one holding c start beyond c, so lo holds c
     const int s = lo;
     const int i = c - stab[8 * s + SQ_FIRST];
     const int len = stab[8 * s + SQ_LEN];
@@ -129,87 +187,187 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
 }
 
 // ---------------------------------------------------------------------------
-// chunk: front end, gates, K K^T / Q K^T, inverse T, P
+// shared MFMA helpers
 // ---------------------------------------------------------------------------
-template <int D>
-struct ChunkSmem {
-  static constexpr int QK_LD = 2 * D + 1;              // q in [0,D), k in [D,2D)
-  static constexpr int QK = kC * QK_LD;
-  static constexpr int LM = 4 * kC * kC;               // up to 4 v-heads' L matrices
-  static constexpr int UNION = QK > LM ? QK : LM;
-  static constexpr int AB_LD = kC + 1;
-  static constexpr int TOTAL = UNION + 2 * kC * AB_LD + 2 * kMaxGroup * kC + 2 * kC;
-  static constexpr size_t BYTES = static_cast<size_t>(TOTAL) * 4;
+// 16x16x4 fp32 MFMA: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// receives D[4*(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// 16x16x32 bf16 MFMA: lane l supplies 8 k-values of row l%16 of A and of
+// column l%16 of B (the same 8 k-values: group l/16), receives as above.
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One packed super-step: A is a packed tile (16 bytes of this lane), B is
+// made of accumulator tiles of a previous product.
+template <bool BF16>
+struct Chain;
+
+template <>
+struct Chain<true> {
+  using Bop = bf16x8_t;
+  __device__ static Bop bop(const f32x4_t& t0, const f32x4_t& t1) {
+    Bop b;
+    b[0] = static_cast<__bf16>(t0[0]); b[1] = static_cast<__bf16>(t0[1]);
+    b[2] = static_cast<__bf16>(t0[2]); b[3] = static_cast<__bf16>(t0[3]);
+    b[4] = static_cast<__bf16>(t1[0]); b[5] = static_cast<__bf16>(t1[1]);
+    b[6] = static_cast<__bf16>(t1[2]); b[7] = static_cast<__bf16>(t1[3]);
+    return b;
+  }
+  __device__ static f32x4_t step(uint4 a, const Bop& b, f32x4_t c) {
+    return mfma32(__builtin_bit_cast(bf16x8_t, a), b, c);
+  }
 };
 
-template <bool BF16>
-__device__ __forceinline__ void ws_store(void* base, size_t i, float v) {
-  if constexpr (BF16) static_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(v);
-  else static_cast<float*>(base)[i] = v;
+template <>
+struct Chain<false> {
+  using Bop = f32x4_t;
+  __device__ static Bop bop(const f32x4_t& t0, const f32x4_t&) { return t0; }
+  __device__ static f32x4_t step(uint4 a, const Bop& b, f32x4_t c) {
+    c = mfma4(__uint_as_float(a.x), b[0], c);
+    c = mfma4(__uint_as_float(a.y), b[1], c);
+    c = mfma4(__uint_as_float(a.z), b[2], c);
+    return mfma4(__uint_as_float(a.w), b[3], c);
+  }
+};
+
+// SiLU with the hardware exp and reciprocal (the front end runs it on every
+// input of every token, so it is kept to five instructions).
+__device__ __forceinline__ float silu_fast(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
 }
 
-// Sliding-window causal conv of one channel over the chunk's tokens.
-// Writes y(r) for r < len through `emit(r, y)`, zeros after.
-template <bool BF16, typename Emit>
-__device__ __forceinline__ void conv_chunk_channel(const PrefillArgs& A, int c, int t0, int len,
-                                                   int seq_start, uint32_t pos0, bool init,
-                                                   int slot, Emit emit) {
-  const int W = A.W, C = A.C, R = A.R;
-  // Fixed-size register arrays indexed with compile-time indices only.
-  float hist[3] = {0.f, 0.f, 0.f};
-  float w[3] = {0.f, 0.f, 0.f};
-  const float wlast = W > 0 ? A.conv_w[c * W + W - 1] : 0.f;
+// acc += A (16x16, row-major at a, stride lda) * B (16x16, row-major at b, stride ldb); fp32.
+__device__ __forceinline__ f32x4_t prod16(const float* a, int lda, const float* b, int ldb,
+                                          f32x4_t acc, int lane) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (t < W - 1) w[t] = A.conv_w[c * W + t];
+  for (int s = 0; s < 4; ++s)
+    acc = mfma4(a[(lane & 15) * lda + 4 * s + (lane >> 4)], b[(4 * s + (lane >> 4)) * ldb + (lane & 15)], acc);
+  return acc;
+}
+
+__device__ __forceinline__ void store16(float* d, int ld, f32x4_t v, float sign, int lane) {
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (i < W - 1) {
-      const int tt = t0 - (W - 1) + i;
-      float v = 0.f;
-      if (tt >= seq_start) {
-        v = load_in<BF16>(A.x, static_cast<size_t>(tt) * C + c);
-      } else if (init) {
-        const int rel = tt - seq_start;  // -(W-1) .. -1
-        v = A.conv_state[(static_cast<size_t>(slot) * R + ring_row(pos0 + static_cast<uint32_t>(rel), R)) * C + c];
-      }
-      hist[i] = v;
+  for (int i = 0; i < 4; ++i) d[(4 * (lane >> 4) + i) * ld + (lane & 15)] = sign * v[i];
+}
+
+// In-place inverse of the unit lower-triangular I + L (64x64, L strictly lower,
+// row stride kLd) by one wave: 16x16 diagonal blocks by forward substitution
+// (lane = block x column), then the off-diagonal blocks level by level with
+// fp32 MFMA:  [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1].
+// tmp: 32 x 33 floats of scratch.
+__device__ void invert_unit_lower64(float* Lt, float* tmp, int lane) {
+  {
+    const int bi = lane >> 4, c = lane & 15;
+    float* Lb = Lt + 16 * bi * kLd + 16 * bi;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) acc = fmaf(-Lb[r * kLd + j], t[j], acc);
+      t[r] = acc;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Lb[r * kLd + c] = t[r];
   }
-  for (int r = 0; r < kC; ++r) {
-    float y = 0.f;
-    if (r < len) {
-      const float xin = load_in<BF16>(A.x, static_cast<size_t>(t0 + r) * C + c);
-      if (W == 0) {
-        y = xin;
-      } else {
-        // taps oldest first, the last one on the current token (same order as the step kernels)
-        float acc = 0.f;
+  // 32x32 level: T10 = -T11 (L10 T00) in both diagonal 32-blocks
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
-          if (t < W - 1) acc = fmaf(w[t], hist[t], acc);
-        acc = fmaf(wlast, xin, acc);
-        y = silu_f(acc);
-        if (W == 4) { hist[0] = hist[1]; hist[1] = hist[2]; hist[2] = xin; }
-        else if (W == 3) { hist[0] = hist[1]; hist[1] = xin; }
-        else if (W == 2) { hist[0] = xin; }
-      }
+  for (int b = 0; b < 2; ++b) {
+    float* o = Lt + 32 * b * kLd + 32 * b;
+    f32x4_t m = prod16(o + 16 * kLd, kLd, o, kLd, f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
+    store16(tmp, 17, m, 1.0f, lane);
+    f32x4_t r = prod16(o + 16 * kLd + 16, kLd, tmp, 17, f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
+    store16(o + 16 * kLd, kLd, r, -1.0f, lane);
+  }
+  // 64x64 level: T_BA = -T_B (C T_A), 32x32 blocks; C is the lower-left block of L
+  const float* C = Lt + 32 * kLd;
+  const float* TA = Lt;
+  const float* TB = Lt + 32 * kLd + 32;
+  f32x4_t m2[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = ct; kt < 2; ++kt)  // T_A[kt][ct] = 0 for kt < ct
+        acc = prod16(C + 16 * rt * kLd + 16 * kt, kLd, TA + 16 * kt * kLd + 16 * ct, kLd, acc, lane);
+      m2[rt][ct] = acc;
     }
-    emit(r, y);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) store16(tmp + 16 * rt * 33 + 16 * ct, 33, m2[rt][ct], 1.0f, lane);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt <= rt; ++kt)  // T_B[rt][kt] = 0 for kt > rt
+        acc = prod16(TB + 16 * rt * kLd + 16 * kt, kLd, tmp + 16 * kt * 33 + 16 * ct, 33, acc, lane);
+      store16(Lt + (32 + 16 * rt) * kLd + 16 * ct, kLd, acc, -1.0f, lane);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ typename Pk<BF16>::E to_e(float v) {
+  if constexpr (BF16) return f32_to_bf16_bits(v);
+  else return v;
+}
+
+// 16 bytes of a packed lane from the EPL values f(0..EPL-1).
+template <bool BF16, typename F>
+__device__ __forceinline__ uint4 pack_lane(F f) {
+  if constexpr (BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(f(2 * i))) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(f(2 * i + 1))) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(f(0)), __float_as_uint(f(1)), __float_as_uint(f(2)), __float_as_uint(f(3)));
   }
 }
+
+// ---------------------------------------------------------------------------
+// chunk: front end, gates, K K^T / Q K^T, inverse T, P  (8 waves)
+// ---------------------------------------------------------------------------
+constexpr int kChunkThreads = 512;
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs A, PrefillLayout Lay) {
-  using Sm = ChunkSmem<D>;
+struct ChunkSmem {
+  static constexpr int QK_LD = 2 * D + 1;               // q in [0,D), k in [D,2D)
+  static constexpr int QK = (kC * QK_LD > 4 * kC * kLd) ? kC * QK_LD : 4 * kC * kLd;  // qk, then L/T
+  static constexpr int PKT = BF16 ? 3 * 4 * Geo<D, BF16>::KSD * kTileBytes / 4 : 0;   // hi, lo, q tiles
+  static constexpr int PK = PKT > 4 * 32 * 33 ? PKT : 4 * 32 * 33;                   // then inverse scratch
+  static constexpr int AB = 2 * kC * kLd;
+  static constexpr int MISC = 2 * kMaxGroup * kC + 2 * kC;
+  static constexpr size_t BYTES = static_cast<size_t>(QK + PK + AB + MISC) * 4;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, PrefillLayout Lay) {
+  using P = Pk<BF16>;
+  using Gm = Geo<D, BF16>;
+  using Sm = ChunkSmem<D, BF16>;
+  using E = typename P::E;
+  constexpr int VE = 16 / sizeof(E);            // channels per 16-byte input vector
+  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* qk = smem;                              // [64][2D+1]   (phase 1)
-  float* Lm = smem;                              // [4][64][64]  (phase 2, reuses qk)
-  float* Am = smem + Sm::UNION;                  // [64][65]  K K^T
-  float* Bm = Am + kC * Sm::AB_LD;               // [64][65]  Q K^T
-  float* gcum = Bm + kC * Sm::AB_LD;             // [G][64]
-  float* bet = gcum + kMaxGroup * kC;            // [G][64]
-  float* inv = bet + kMaxGroup * kC;             // [2][64]
+  float* qk = smem;                               // [64][2D+1] raw conv outputs of q | k
+  float* Lt = smem;                               // [4][64][65] L -> T   (per-head phase)
+  uint4* pk = reinterpret_cast<uint4*>(smem + Sm::QK);  // packed k_hi, k_lo, q tiles (bf16 only)
+  float* tmpw = smem + Sm::QK;                    // [4][32][33] inverse scratch (per-head phase)
+  float* Am = smem + Sm::QK + Sm::PK;             // [64][65] K K^T (normalised)
+  float* Bm = Am + kC * kLd;                      // [64][65] Q K^T (normalised, q_scale)
+  float* gcum = Bm + kC * kLd;                    // [8][64]
+  float* bet = gcum + kMaxGroup * kC;             // [8][64]
+  float* inv = bet + kMaxGroup * kC;              // [2][64]  q and k scale factors
 
   const int chunk = blockIdx.x;
   const int kh = blockIdx.y;
@@ -222,50 +380,156 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs A, PrefillLayout
   const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
   const int slot = se[SQ_SLOT];
   const int seq_start = se[SQ_START];
-  const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk;
+  const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, C = A.C, R = A.R, W = A.W;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NCH = (2 + G) * D;                    // channels of this k-head: q | k | v of its v-heads
+  const E* x = static_cast<const E*>(A.x);
+  char* kqb = static_cast<char*>(A.workspace) + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
+  auto headb = [&](int h) {
+    return static_cast<char*>(A.workspace) + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
+  };
+  auto xchan = [&](int cc) {
+    return cc < D ? kh * D + cc : (cc < 2 * D ? Hk * D + kh * D + (cc - D) : 2 * Hk * D + kh * G * D + (cc - 2 * D));
+  };
 
-  // ---- q, k channels of this k-head: conv + SiLU into LDS ----
-  for (int cc = tid; cc < 2 * D; cc += blockDim.x) {
-    const int c = cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D);
-    conv_chunk_channel<BF16>(A, c, t0, len, seq_start, pos0, init, slot,
-                             [&](int r, float y) { qk[r * Sm::QK_LD + cc] = y; });
+  // ---- gates: one wave per v-head, lane = token, fixed-order inclusive scan ----
+  for (int hi = wave; hi < G; hi += kChunkThreads / 64) {
+    const int h = kh * G + hi;
+    float g = 0.f, bb = 0.f;
+    if (lane < len) {
+      const size_t i = static_cast<size_t>(t0 + lane) * Hv + h;
+      g = -softplus_f(load_in<BF16>(A.a, i));
+      bb = sigmoid_f(load_in<BF16>(A.b, i));
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float up = __shfl_up(g, off, 64);
+      if (lane >= off) g += up;
+    }
+    gcum[hi * kC + lane] = g;
+    bet[hi * kC + lane] = bb;
+    const float glast = __shfl(g, 63, 64);
+    const float eg = __expf(g);
+    float* gw = reinterpret_cast<float*>(headb(h) + Gm::GATE_OFF);
+    gw[lane] = eg;
+    gw[kC + lane] = bb * eg;
+    gw[2 * kC + lane] = __expf(glast - g);
+    gw[3 * kC + lane] = __expf(glast);
   }
-  // ---- v channels of the k-head's v-heads: straight to the workspace ----
-  for (int cc = tid; cc < G * D; cc += blockDim.x) {
-    const int h = kh * G + cc / D;
-    const int dv = cc % D;
-    const int c = 2 * Hk * D + h * D + dv;
-    void* vb = static_cast<char*>(A.workspace) + Lay.v;
-    const size_t base = (static_cast<size_t>(chunk) * Hv + h) * kC * D + dv;
-    conv_chunk_channel<BF16>(A, c, t0, len, seq_start, pos0, init, slot,
-                             [&](int r, float y) { ws_store<BF16>(vb, base + static_cast<size_t>(r) * D, y); });
-  }
-  // ---- gates: g = -softplus(a), beta = sigmoid(b), cumulative G ----
-  if (tid < G) {
-    const int h = kh * G + tid;
-    float Gc = 0.f;
-    float* wg = ws_ptr<float>(A.workspace, Lay.g) + (static_cast<size_t>(chunk) * Hv + h) * kC;
-    float* wb = ws_ptr<float>(A.workspace, Lay.beta) + (static_cast<size_t>(chunk) * Hv + h) * kC;
-    for (int r = 0; r < kC; ++r) {
-      float g = 0.f, bb = 0.f;
-      if (r < len) {
-        const size_t i = static_cast<size_t>(t0 + r) * Hv + h;
-        g = -softplus_f(load_in<BF16>(A.a, i));
-        bb = sigmoid_f(load_in<BF16>(A.b, i));
+
+  __syncthreads();  // betas are in LDS: V is stored pre-scaled by beta
+
+  // ---- conv + SiLU: item = (VE channels, 16 tokens), the 19-row window in registers ----
+  const int nvec = NCH / VE;
+  for (int item = tid; item < 4 * nvec; item += kChunkThreads) {
+    const int q = item / nvec, cc0 = (item - q * nvec) * VE;
+    const int c0 = xchan(cc0);
+    const int tq = 16 * q;                        // first token of this quarter
+    // raw rows: tokens t0+tq-3 .. t0+tq+15 (row i <-> token t0+tq-3+i),
+    // clamped into the sequence and the chunk so every load is valid
+    uint4 raw[19];
+#pragma unroll
+    for (int i = 0; i < 19; ++i) {
+      const int t = min(max(t0 + tq - 3 + i, seq_start), t0 + len - 1);
+      raw[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * C + c0);
+    }
+    float w[VE][4];
+    if (W == 4) {
+#pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        const float4 w4 = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
+        w[v][0] = w4.x; w[v][1] = w4.y; w[v][2] = w4.z; w[v][3] = w4.w;
       }
-      Gc += g;
-      gcum[tid * kC + r] = Gc;
-      bet[tid * kC + r] = bb;
-      wg[r] = Gc;
-      wb[r] = bb;
+    }
+    auto elem = [&](const uint4& r, int v) -> float {
+      if constexpr (BF16) {
+        const uint32_t wv = (v >> 1) == 0 ? r.x : (v >> 1) == 1 ? r.y : (v >> 1) == 2 ? r.z : r.w;
+        return __uint_as_float((v & 1) ? (wv & 0xffff0000u) : (wv << 16));
+      } else {
+        return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
+      }
+    };
+    // the three rows before the quarter: x, or the ring / zero before the sequence
+    float hist[VE][3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int t = t0 + tq - 3 + i;
+#pragma unroll
+      for (int v = 0; v < VE; ++v) hist[v][i] = elem(raw[i], v);
+      if (t < seq_start) {
+        if (init) {
+          const float* rr = A.conv_state + (static_cast<size_t>(slot) * R +
+                                            ring_row(pos0 + static_cast<uint32_t>(t - seq_start), R)) * C + c0;
+#pragma unroll
+          for (int v = 0; v < VE; ++v) hist[v][i] = rr[v];
+        } else {
+#pragma unroll
+          for (int v = 0; v < VE; ++v) hist[v][i] = 0.f;
+        }
+      }
+    }
+    const bool is_v = cc0 >= 2 * D;
+    const int hv = is_v ? (cc0 - 2 * D) / D : 0;  // v-head within the group
+    const int dv0 = is_v ? (cc0 - 2 * D) % D : 0;
+    E* vcb = reinterpret_cast<E*>(headb(kh * G + hv) + Gm::VC_OFF);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {              // 4 groups of 4 tokens
+      float y[VE][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;                 // token within the quarter
+        const bool valid = tq + r < len;
+#pragma unroll
+        for (int v = 0; v < VE; ++v) {
+          const float xin = elem(raw[3 + r], v);
+          float yy;
+          if (W == 4) {
+            float acc = w[v][0] * hist[v][0];
+            acc = fmaf(w[v][1], hist[v][1], acc);
+            acc = fmaf(w[v][2], hist[v][2], acc);
+            acc = fmaf(w[v][3], xin, acc);
+            yy = silu_fast(acc);
+            hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
+          } else {
+            yy = xin;
+          }
+          y[v][i] = valid ? yy : 0.f;
+        }
+      }
+      if (!is_v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < VE; ++v) qk[(tq + 4 * g4 + i) * Sm::QK_LD + cc0 + v] = y[v][i];
+      } else {
+        // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i;
+        // stored as beta * v
+        const float4 bq = *reinterpret_cast<const float4*>(bet + hv * kC + tq + 4 * g4);
+#pragma unroll
+        for (int v = 0; v < VE; ++v) {
+          y[v][0] *= bq.x; y[v][1] *= bq.y; y[v][2] *= bq.z; y[v][3] *= bq.w;
+        }
+#pragma unroll
+        for (int v = 0; v < VE; ++v) {
+          const int dv = dv0 + v;
+          E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
+          if constexpr (BF16) {
+            uint2 pkd;
+            pkd.x = static_cast<uint32_t>(f32_to_bf16_bits(y[v][0])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[v][1])) << 16);
+            pkd.y = static_cast<uint32_t>(f32_to_bf16_bits(y[v][2])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[v][3])) << 16);
+            *reinterpret_cast<uint2*>(dst) = pkd;
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
+          }
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- L2 norm of q and k per token (fixed reduction order) ----
+  // ---- L2 norm factors of q and k per token (fixed reduction order) ----
   const bool norm = (A.flags & GDN_FLAG_L2NORM_QK) != 0;
-  for (int r = wave * 16; r < wave * 16 + 16; ++r) {
+  for (int r = wave * 8; r < wave * 8 + 8; ++r) {
     float sq = 0.f, sk = 0.f;
     for (int d = lane; d < D; d += 64) {
       const float qv = qk[r * Sm::QK_LD + d];
@@ -281,168 +545,151 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs A, PrefillLayout
     }
   }
   __syncthreads();
-  for (int e = tid; e < kC * 2 * D; e += blockDim.x) {
-    const int r = e / (2 * D), cc = e % (2 * D);
-    qk[r * Sm::QK_LD + cc] *= inv[(cc >= D ? kC : 0) + r];
+  auto qn = [&](int r, int d) { return qk[r * Sm::QK_LD + d] * inv[r]; };
+  auto kn = [&](int r, int d) { return qk[r * Sm::QK_LD + D + d] * inv[kC + r]; };
+
+  // ---- packed K, Q (rows tok, k = d) and K^T (rows d, k = tok) to the workspace ----
+  // (bf16: also k_hi, k_lo, q tiles into LDS for the K K^T / Q K^T products)
+  for (int u = tid; u < 4 * KSD * 64; u += kChunkThreads) {
+    const int tile = u >> 6, ln = u & 63;
+    const int mt = tile / KSD, ks = tile % KSD;
+    const int row = 16 * mt + (ln & 15), g = ln >> 4;
+    auto kof = [&](int e) { return ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3); };
+    const uint4 kw = pack_lane<BF16>([&](int e) { const int k = kof(e); return k < D ? kn(row, k) : 0.f; });
+    const uint4 qw = pack_lane<BF16>([&](int e) { const int k = kof(e); return k < D ? qn(row, k) : 0.f; });
+    reinterpret_cast<uint4*>(kqb + (Gm::KA + tile) * kTileBytes)[ln] = kw;
+    reinterpret_cast<uint4*>(kqb + (Gm::QA + tile) * kTileBytes)[ln] = qw;
+    if constexpr (BF16) {
+      const uint4 lw = pack_lane<BF16>([&](int e) {
+        const int k = kof(e);
+        if (k >= D) return 0.f;
+        const float v = kn(row, k);
+        return v - bf16_bits_to_f32(f32_to_bf16_bits(v));
+      });
+      pk[(0 * 4 * KSD + tile) * 64 + ln] = kw;
+      pk[(1 * 4 * KSD + tile) * 64 + ln] = lw;
+      pk[(2 * 4 * KSD + tile) * 64 + ln] = qw;
+    }
+  }
+  for (int u = tid; u < NT * KSC * 64; u += kChunkThreads) {
+    const int tile = u >> 6, ln = u & 63;
+    const int mt = tile / KSC, ks = tile % KSC;
+    const int dk = 16 * mt + (ln & 15), g = ln >> 4;
+    const uint4 w4 = pack_lane<BF16>([&](int e) { return kn(ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3), dk); });
+    reinterpret_cast<uint4*>(kqb + (Gm::KTA + tile) * kTileBytes)[ln] = w4;
   }
   __syncthreads();
 
-  // ---- q, k, k^T to the workspace ----
-  {
-    void* wq = static_cast<char*>(A.workspace) + Lay.q;
-    void* wk = static_cast<char*>(A.workspace) + Lay.k;
-    void* wkt = static_cast<char*>(A.workspace) + Lay.kt;
-    const size_t base = (static_cast<size_t>(chunk) * Hk + kh) * kC * D;
-    for (int e = tid; e < kC * D; e += blockDim.x) {
-      const int r = e / D, d = e % D;
-      ws_store<BF16>(wq, base + e, qk[r * Sm::QK_LD + d]);
-      ws_store<BF16>(wk, base + e, qk[r * Sm::QK_LD + D + d]);
-      const int d2 = e / kC, r2 = e % kC;
-      ws_store<BF16>(wkt, base + e, qk[r2 * Sm::QK_LD + D + d2]);
-    }
-  }
-
-  // ---- A = K K^T and B = Q K^T (lower triangles incl. diagonal), fp32 MFMA ----
-  // 16x16x4 f32 MFMA: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
-  // receives D[4*(l/16)+i][l%16], i = 0..3.
-  for (int task = wave; task < 20; task += 4) {
+  // ---- A = K K^T and B = Q K^T (lower 16x16 tiles incl. the diagonal) ----
+  for (int task = wave; task < 20; task += kChunkThreads / 64) {
     const int which = task / 10;  // 0: K K^T, 1: Q K^T
     int t = task % 10, ti = 0;
     while (t > ti) { t -= ti + 1; ++ti; }
     const int tj = t;
-    const float* lhs = qk + (which == 0 ? D : 0);
-    const float* rhs = qk + D;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const int ra = ti * 16 + (lane & 15), rb = tj * 16 + (lane & 15), kk = lane >> 4;
-    for (int k0 = 0; k0 < D; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lhs[ra * Sm::QK_LD + k0 + kk],
-                                                 rhs[rb * Sm::QK_LD + k0 + kk], acc, 0, 0, 0);
+    if constexpr (BF16) {
+      // K K^T (which feeds the inverse) sums hi*hi + hi*lo + lo*hi for about
+      // fp32 accuracy; Q K^T (stored as bf16) takes one product.  A packed
+      // K tile is also the B operand of K^T (same lanes, same k order).
+      const uint4* khi = pk;
+      const uint4* klo = pk + 4 * KSD * 64;
+      const uint4* qq = pk + 2 * 4 * KSD * 64;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, khi[(tj * KSD + ks) * 64 + lane]);
+        if (which == 0) {
+          const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, khi[(ti * KSD + ks) * 64 + lane]);
+          const bf16x8_t al = __builtin_bit_cast(bf16x8_t, klo[(ti * KSD + ks) * 64 + lane]);
+          const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, klo[(tj * KSD + ks) * 64 + lane]);
+          acc = mfma32(ah, bh, acc);
+          acc = mfma32(ah, bl, acc);
+          acc = mfma32(al, bh, acc);
+        } else {
+          acc = mfma32(__builtin_bit_cast(bf16x8_t, qq[(ti * KSD + ks) * 64 + lane]), bh, acc);
+        }
+      }
+    } else {
+      const int ra = ti * 16 + (lane & 15), rb = tj * 16 + (lane & 15), kk = lane >> 4;
+      for (int k0 = 0; k0 < D; k0 += 4) {
+        const float av = which == 0 ? kn(ra, k0 + kk) : qn(ra, k0 + kk);
+        acc = mfma4(av, kn(rb, k0 + kk), acc);
+      }
+    }
     float* out = which == 0 ? Am : Bm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[(ti * 16 + (lane >> 4) * 4 + i) * Sm::AB_LD + tj * 16 + (lane & 15)] = acc[i];
+    for (int i = 0; i < 4; ++i) out[(ti * 16 + (lane >> 4) * 4 + i) * kLd + tj * 16 + (lane & 15)] = acc[i];
   }
   __syncthreads();
 
-  // ---- per v-head: L (LDS), P (workspace), T = (I+L)^{-1} (workspace) ----
-  void* wt = static_cast<char*>(A.workspace) + Lay.t;
-  void* wp = static_cast<char*>(A.workspace) + Lay.p;
+  // ---- per v-head: L (LDS), P and T (packed, workspace) ----
   for (int hg0 = 0; hg0 < G; hg0 += 4) {
     const int nh = min(4, G - hg0);
-    for (int e = tid; e < nh * kC * kC; e += blockDim.x) {
+    for (int e = tid; e < nh * kC * kC; e += kChunkThreads) {
       const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
       const float* gc = gcum + (hg0 + i) * kC;
-      Lm[e] = j < r ? bet[(hg0 + i) * kC + r] * expf(gc[r] - gc[j]) * Am[r * Sm::AB_LD + j] : 0.f;
-      const float pv = j <= r ? expf(gc[r] - gc[j]) * Bm[r * Sm::AB_LD + j] : 0.f;
-      const int h = kh * G + hg0 + i;
-      ws_store<BF16>(wp, (static_cast<size_t>(chunk) * Hv + h) * kC * kC + r * kC + j, pv);
+      Lt[i * kC * kLd + r * kLd + j] = j < r ? bet[(hg0 + i) * kC + r] * __expf(gc[r] - gc[j]) * Am[r * kLd + j] : 0.f;
+    }
+    for (int u = tid; u < nh * 4 * KSC * 64; u += kChunkThreads) {
+      const int i = u / (4 * KSC * 64), tile = (u >> 6) % (4 * KSC), ln = u & 63;
+      const int mt = tile / KSC, ks = tile % KSC;
+      const int r = 16 * mt + (ln & 15), g = ln >> 4;
+      const float* gc = gcum + (hg0 + i) * kC;
+      const uint4 w4 = pack_lane<BF16>([&](int e) {
+        const int j = ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        return j <= r ? __expf(gc[r] - gc[j]) * Bm[r * kLd + j] : 0.f;
+      });
+      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::PA + tile) * kTileBytes)[ln] = w4;
     }
     __syncthreads();
-    if (wave < nh) {
-      // Forward substitution for column `lane` of T: T[r][c] = d_rc - sum_{j<r} L[r][j] T[j][c].
-      const float* Lw = Lm + wave * kC * kC;
-      float t[kC];
-#pragma unroll
-      for (int r = 0; r < kC; ++r) {
-        float acc = (r == lane) ? 1.0f : 0.0f;
-        const float4* Lr = reinterpret_cast<const float4*>(Lw + r * kC);
-#pragma unroll
-        for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
-          const float4 l4 = Lr[j4];
-          if (4 * j4 + 0 < r) acc = fmaf(-l4.x, t[4 * j4 + 0], acc);
-          if (4 * j4 + 1 < r) acc = fmaf(-l4.y, t[4 * j4 + 1], acc);
-          if (4 * j4 + 2 < r) acc = fmaf(-l4.z, t[4 * j4 + 2], acc);
-          if (4 * j4 + 3 < r) acc = fmaf(-l4.w, t[4 * j4 + 3], acc);
-        }
-        t[r] = acc;
-      }
-      const int h = kh * G + hg0 + wave;
-      const size_t base = (static_cast<size_t>(chunk) * Hv + h) * kC * kC;
-#pragma unroll
-      for (int r = 0; r < kC; ++r) ws_store<BF16>(wt, base + r * kC + lane, t[r]);
+    if (wave < nh) invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
+    __syncthreads();
+    for (int u = tid; u < nh * 4 * KSC * 64; u += kChunkThreads) {
+      const int i = u / (4 * KSC * 64), tile = (u >> 6) % (4 * KSC), ln = u & 63;
+      const int mt = tile / KSC, ks = tile % KSC;
+      const int r = 16 * mt + (ln & 15), g = ln >> 4;
+      const float* Ti = Lt + i * kC * kLd;
+      const uint4 w4 = pack_lane<BF16>([&](int e) { return Ti[r * kLd + ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3)]; });
+      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::TA + tile) * kTileBytes)[ln] = w4;
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// state: sequential chunk loop per (sequence, v-head, d_v block)
+// chain: sequential chunk loop, one wave per 16 rows of d_v
 // ---------------------------------------------------------------------------
-template <bool BF16>
-struct Mma;
-
-// 16x16x32 bf16 MFMA: lane l supplies A[l%16][8*(l/16) + 0..7] and
-// B[8*(l/16) + 0..7][l%16]; it receives D[4*(l/16) + i][l%16], i = 0..3.
-template <>
-struct Mma<true> {
-  using E = uint16_t;
-  using Op = bf16x8_t;
-  static constexpr int KSTEP = 32;
-  static constexpr int KPL = 8;
-  static constexpr int PAD = 8;
-  __device__ static Op load(const E* p) { return *reinterpret_cast<const Op*>(p); }
-  __device__ static f32x4_t mma(Op a, Op b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static E cvt(float f) { return f32_to_bf16_bits(f); }
-  __device__ static float back(E e) { return bf16_bits_to_f32(e); }
+template <int D, bool BF16, int CW>
+struct ChainSmem {
+  using Gm = Geo<D, BF16>;
+  static constexpr size_t KQ = Gm::KQ_BYTES;
+  static constexpr size_t TP = 8 * Gm::KSC * kTileBytes;
+  static constexpr size_t VC = CW * 4 * Pk<BF16>::VC_BYTES;
+  static constexpr size_t GATES = Gm::GATE_BYTES;
+  static constexpr size_t BUF = KQ + TP + VC + GATES;
+  static constexpr int UNITS = static_cast<int>(BUF / 16);           // 16-byte units per buffer
+  static constexpr int NBUF = 2 * BUF <= 150 * 1024 ? 2 : 1;
+  static constexpr size_t BYTES = NBUF * BUF;
 };
 
-// 16x16x4 f32 MFMA: lane l supplies A[l%16][l/16] and B[l/16][l%16].
-template <>
-struct Mma<false> {
-  using E = float;
-  using Op = float;
-  static constexpr int KSTEP = 4;
-  static constexpr int KPL = 1;
-  static constexpr int PAD = 4;
-  __device__ static Op load(const E* p) { return *p; }
-  __device__ static f32x4_t mma(Op a, Op b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-  __device__ static E cvt(float f) { return f; }
-  __device__ static float back(E e) { return e; }
-};
+template <int D, bool BF16, int CW>
+__global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, PrefillLayout Lay) {
+  using P = Pk<BF16>;
+  using Gm = Geo<D, BF16>;
+  using Sm = ChainSmem<D, BF16, CW>;
+  using Ch = Chain<BF16>;
+  using E = typename P::E;
+  using Bop = typename Ch::Bop;
+  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT;
+  constexpr int TPS = P::SK / 16;                 // accumulator tiles per packed super-step
+  constexpr int U_KQ = static_cast<int>(Sm::KQ / 16);
+  constexpr int U_TP = U_KQ + static_cast<int>(Sm::TP / 16);
+  constexpr int U_VC = U_TP + static_cast<int>(Sm::VC / 16);
+  __shared__ __attribute__((aligned(1024))) char lds0[Sm::BUF];
+  __shared__ __attribute__((aligned(1024))) char lds1[Sm::NBUF == 2 ? Sm::BUF : 16];
 
-template <int D>
-struct StateShape {
-  static constexpr int DVT = D >= 64 ? 32 : 16;        // d_v rows per workgroup
-  static constexpr int NDT = DVT / 16;                 // 16-row tiles of the block
-  static constexpr int NKT = D / 16;                   // 16-column tiles of d_k
-  static constexpr int NS = (NDT * NKT + 3) / 4;       // state tiles per wave
-};
-
-// Operand of a 16-row tile at (row0, k0) of a row-major matrix with leading dimension ld.
-// KLEN is the length of the contracted dimension when it is shorter than one
-// MFMA k-step (d = 16 with the 32-deep bf16 MFMA): lanes whose k-range lies
-// beyond it supply zeros and read nothing.
-template <bool BF16, int KLEN = 1 << 30>
-__device__ __forceinline__ typename Mma<BF16>::Op op_at(const typename Mma<BF16>::E* m, int ld,
-                                                        int row0, int k0, int lane) {
-  using M = Mma<BF16>;
-  const int kk = k0 + (lane >> 4) * M::KPL;
-  if constexpr (KLEN < M::KSTEP) {
-    if (kk >= KLEN) return typename M::Op{};
-  }
-  return M::load(m + static_cast<size_t>(row0 + (lane & 15)) * ld + kk);
-}
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void state_kernel(PrefillArgs A, PrefillLayout Lay) {
-  using M = Mma<BF16>;
-  using E = typename M::E;
-  using Sh = StateShape<D>;
-  constexpr int DVT = Sh::DVT, NDT = Sh::NDT, NKT = Sh::NKT, NS = Sh::NS;
-  constexpr int SLD = D + M::PAD;       // S block [DVT][D]
-  constexpr int TLD = kC + M::PAD;      // R, U, Ut blocks [DVT][64]
-  __shared__ __attribute__((aligned(16))) E S_l[DVT * SLD];
-  __shared__ __attribute__((aligned(16))) E R_l[DVT * TLD];
-  __shared__ __attribute__((aligned(16))) E U_l[DVT * TLD];
-  __shared__ __attribute__((aligned(16))) E Ut_l[DVT * TLD];
-  __shared__ float g_l[2][kC];
-  __shared__ float b_l[2][kC];
-
-  const int s = blockIdx.x, h = blockIdx.y, dv0 = blockIdx.z * DVT;
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dvt = blockIdx.z * CW + wave;        // this wave's 16 rows of d_v
   const int32_t* se = ws_ptr<int32_t>(A.workspace, Lay.seq_tab) + 8 * s;
   if (!(se[SQ_FLAGS] & SQF_VALID)) return;
   const bool init = (se[SQ_FLAGS] & SQF_INIT) != 0;
@@ -450,147 +697,202 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs A, PrefillLayout
   const int seq_start = se[SQ_START], len = se[SQ_LEN];
   const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, kh = h / G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* ctab = ws_ptr<int32_t>(A.workspace, Lay.chunk_tab);
-  const E* wq = ws_ptr<const E>(A.workspace, Lay.q);
-  const E* wk = ws_ptr<const E>(A.workspace, Lay.k);
-  const E* wkt = ws_ptr<const E>(A.workspace, Lay.kt);
-  const E* wv = ws_ptr<const E>(A.workspace, Lay.v);
-  const E* wT = ws_ptr<const E>(A.workspace, Lay.t);
-  const E* wP = ws_ptr<const E>(A.workspace, Lay.p);
-  const float* wg = ws_ptr<const float>(A.workspace, Lay.g);
-  const float* wb = ws_ptr<const float>(A.workspace, Lay.beta);
+  const int g = lane >> 4, col = lane & 15;
 
-  // ---- the state block in accumulators (fp32) and in LDS (operand type) ----
-  float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D;
-  f32x4_t Sacc[NS];
+  // ---- S^T slice in accumulators: tile i holds S^T[16i + 4g + e][16 dvt + col] ----
+  float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
+  f32x4_t st[NT];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int tt = wave + 4 * i;
-    Sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (tt < NDT * NKT) {
-      const int dvt = tt / NKT, dkt = tt % NKT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dv = dvt * 16 + (lane >> 4) * 4 + e, dk = dkt * 16 + (lane & 15);
-        const float v = init ? Sglob[static_cast<size_t>(dv0 + dv) * D + dk] : 0.f;
-        Sacc[i][e] = v;
-        S_l[dv * SLD + dk] = M::cvt(v);
-      }
+  for (int i = 0; i < NT; ++i) {
+    if (init) {
+      const float4 v = *reinterpret_cast<const float4*>(Sglob + 16 * i + 4 * g);
+      st[i] = f32x4_t{v.x, v.y, v.z, v.w};
+    } else {
+      st[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
 
-  const int tok = 16 * wave + (lane & 15);   // this lane's token column in steps 1-4
-  for (int ci = 0; ci < nc; ++ci) {
-    const int chunk = first + ci;
-    const int t0 = ctab[4 * chunk + 1], clen = ctab[4 * chunk + 2];
-    const int buf = ci & 1;
-    if (tid < kC) {
-      g_l[buf][tid] = wg[(static_cast<size_t>(chunk) * Hv + h) * kC + tid];
-      b_l[buf][tid] = wb[(static_cast<size_t>(chunk) * Hv + h) * kC + tid];
-    }
-    __syncthreads();  // B0: S_l and gates ready; U_l, Ut_l free
-
-    const E* Kc = wk + (static_cast<size_t>(chunk) * Hk + kh) * kC * D;
-    const E* Qc = wq + (static_cast<size_t>(chunk) * Hk + kh) * kC * D;
-    const E* KTc = wkt + (static_cast<size_t>(chunk) * Hk + kh) * D * kC;
-    const E* Vc = wv + (static_cast<size_t>(chunk) * Hv + h) * kC * D;
-    const E* Tc = wT + (static_cast<size_t>(chunk) * Hv + h) * kC * kC;
-    const E* Pc = wP + (static_cast<size_t>(chunk) * Hv + h) * kC * kC;
-    const float eG = expf(g_l[buf][tok]);
-    const float bt = b_l[buf][tok];
-
-    // steps 1 and 4a: X^T = S K^T and Y^T = S Q^T for this wave's 16 tokens;
-    // step 2: R^T = (V^T - X^T diag(e^G)) diag(beta) -> LDS
-    f32x4_t Y[NDT];
+  // Staging of one chunk into one LDS buffer with direct global->LDS loads:
+  // the packed K/Q/K^T block of the k-head, the T/P tiles, this workgroup's V
+  // tiles and the gate factors of the head.  The two buffers are distinct LDS
+  // arrays, so loads landing in one never make the compiler wait before
+  // reading the other.
+  const char* wsb = static_cast<const char*>(A.workspace);
+  auto stage = [&](int chunk, char* base) {
+    const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
+    const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
+    const char* vcb = hb + Gm::VC_OFF + static_cast<size_t>(blockIdx.z) * CW * 4 * P::VC_BYTES;
+    constexpr int NBLK = static_cast<int>((Sm::BUF + 1023) / 1024);
 #pragma unroll
-    for (int dvt = 0; dvt < NDT; ++dvt) {
-      f32x4_t X = {0.f, 0.f, 0.f, 0.f};
-      f32x4_t Yt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
-        const auto a = op_at<BF16, D>(S_l, SLD, dvt * 16, k0, lane);
-        X = M::mma(a, op_at<BF16, D>(Kc, D, 16 * wave, k0, lane), X);
-        Yt = M::mma(a, op_at<BF16, D>(Qc, D, 16 * wave, k0, lane), Yt);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dv = dvt * 16 + (lane >> 4) * 4 + e;
-        const float vv = M::back(Vc[static_cast<size_t>(tok) * D + dv0 + dv]);
-        R_l[dv * TLD + tok] = M::cvt(bt * (vv - eG * X[e]));
-        Y[dvt][e] = eG * Yt[e];
+    for (int j = 0; j < (NBLK + CW - 1) / CW; ++j) {
+      const int b = wave + j * CW;                  // 1 KB block of the buffer
+      if (b < NBLK) {
+        const int u = b * 64 + lane;                // 16-byte unit
+        const char* src = u < U_KQ ? kq + 16 * u
+                        : u < U_TP ? hb + 16 * (u - U_KQ)
+                        : u < U_VC ? vcb + 16 * (u - U_TP)
+                                   : hb + Gm::GATE_OFF + 16 * (u - U_VC);
+        if (u < Sm::UNITS)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src),
+                                           (__attribute__((address_space(3))) void*)(base + b * 1024), 16, 0, 0);
       }
     }
-    __syncthreads();  // B1: R_l complete
+  };
+  auto wait_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
+    lds_barrier();                  // ... and everyone else's
+  };
 
-    // step 3: U^T = R^T T^T (T lower triangular: j < 16*wave + 16)
-    const int kend = 16 * wave + 16;
-    const float dec = expf(g_l[buf][kC - 1] - g_l[buf][tok]);
+  // One chunk step from LDS buffer buf; O returned in registers.
+  auto compute = [&](const char* base, f32x4_t (&O)[4]) {
+    const uint4* kq = reinterpret_cast<const uint4*>(base);
+    const uint4* tp = reinterpret_cast<const uint4*>(base + Sm::KQ);
+    const E* vc = reinterpret_cast<const E*>(base + Sm::KQ + Sm::TP) + wave * 4 * 256;
+    const float* gt = reinterpret_cast<const float*>(base + Sm::KQ + Sm::TP + Sm::VC);
+    auto tileA = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
+
+    // B operands of S^T (d_k in packed order)
+    Bop bS[KSD];
 #pragma unroll
-    for (int dvt = 0; dvt < NDT; ++dvt) {
-      f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < kend; k0 += M::KSTEP)
-        U = M::mma(op_at<BF16>(R_l, TLD, dvt * 16, k0, lane), op_at<BF16>(Tc, kC, 16 * wave, k0, lane), U);
+    for (int ks = 0; ks < KSD; ++ks) {
+      const int i0 = ks * TPS;
+      bS[ks] = Ch::bop(st[i0], (TPS == 2 && i0 + 1 < NT) ? st[(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
+    }
+    // X = K S^T and Y = Q S^T for the 4 token tiles
+    f32x4_t X[4], Y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dv = dvt * 16 + (lane >> 4) * 4 + e;
-        U_l[dv * TLD + tok] = M::cvt(U[e]);
-        Ut_l[dv * TLD + tok] = M::cvt(U[e] * dec);
+    for (int mt = 0; mt < 4; ++mt) {
+      X[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        X[mt] = Ch::step(tileA(kq + Gm::KA * 64, mt * KSD + ks), bS[ks], X[mt]);
+        Y[mt] = Ch::step(tileA(kq + Gm::QA * 64, mt * KSD + ks), bS[ks], Y[mt]);
       }
     }
-    __syncthreads();  // B2: U_l, Ut_l complete
-
-    // step 4b: O^T = Y^T + U^T P^T (P lower triangular), written for valid tokens
+    // R = beta V - (beta e^G) X for this lane's tokens 16 mt + 4 g + i
+    f32x4_t Rt[4];
 #pragma unroll
-    for (int dvt = 0; dvt < NDT; ++dvt) {
-      f32x4_t O = Y[dvt];
-      for (int k0 = 0; k0 < kend; k0 += M::KSTEP)
-        O = M::mma(op_at<BF16>(U_l, TLD, dvt * 16, k0, lane), op_at<BF16>(Pc, kC, 16 * wave, k0, lane), O);
-      if (tok < clen) {
-        const size_t ob = (static_cast<size_t>(t0 + tok) * Hv + h) * D + dv0 + dvt * 16 + (lane >> 4) * 4;
-        if constexpr (BF16) {
-          uint2 pk;
-          pk.x = static_cast<uint32_t>(f32_to_bf16_bits(O[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(O[1])) << 16);
-          pk.y = static_cast<uint32_t>(f32_to_bf16_bits(O[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(O[3])) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(A.o) + ob) = pk;
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(A.o) + ob) = make_float4(O[0], O[1], O[2], O[3]);
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 c1 = *reinterpret_cast<const float4*>(gt + kC + 16 * mt + 4 * g);
+      float vv[4];
+      if constexpr (BF16) {
+        const uint2 r2 = *reinterpret_cast<const uint2*>(vc + mt * 256 + lane * 4);
+        vv[0] = __uint_as_float(r2.x << 16); vv[1] = __uint_as_float(r2.x & 0xffff0000u);
+        vv[2] = __uint_as_float(r2.y << 16); vv[3] = __uint_as_float(r2.y & 0xffff0000u);
+      } else {
+        const float4 r4 = *reinterpret_cast<const float4*>(vc + mt * 256 + lane * 4);
+        vv[0] = r4.x; vv[1] = r4.y; vv[2] = r4.z; vv[3] = r4.w;
+      }
+      Rt[mt][0] = fmaf(-c1.x, X[mt][0], vv[0]);
+      Rt[mt][1] = fmaf(-c1.y, X[mt][1], vv[1]);
+      Rt[mt][2] = fmaf(-c1.z, X[mt][2], vv[2]);
+      Rt[mt][3] = fmaf(-c1.w, X[mt][3], vv[3]);
+    }
+    // U = T R (T lower triangular: token tile mt needs j < 16 (mt + 1))
+    Bop bR[KSC];
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) bR[ks] = Ch::bop(Rt[ks * TPS], Rt[(ks * TPS + 1) % 4]);
+    f32x4_t U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      U[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks)
+        if (ks * P::SK < 16 * (mt + 1)) U[mt] = Ch::step(tileA(tp + Gm::TA * 64, mt * KSC + ks), bR[ks], U[mt]);
+    }
+    // O = diag(e^G) Y + P U;  Ut = diag(e^{G_last - G}) U
+    f32x4_t Ut[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 dc = *reinterpret_cast<const float4*>(gt + 2 * kC + 16 * mt + 4 * g);
+      Ut[mt] = U[mt] * f32x4_t{dc.x, dc.y, dc.z, dc.w};
+    }
+    Bop bU[KSC], bUt[KSC];
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) {
+      bU[ks] = Ch::bop(U[ks * TPS], U[(ks * TPS + 1) % 4]);
+      bUt[ks] = Ch::bop(Ut[ks * TPS], Ut[(ks * TPS + 1) % 4]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 eg = *reinterpret_cast<const float4*>(gt + 16 * mt + 4 * g);
+      f32x4_t o = Y[mt] * f32x4_t{eg.x, eg.y, eg.z, eg.w};
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks)
+        if (ks * P::SK < 16 * (mt + 1)) o = Ch::step(tileA(tp + Gm::PA * 64, mt * KSC + ks), bU[ks], o);
+      O[mt] = o;
+    }
+    // S^T <- e^{G_last} S^T + K^T Ut
+    const float eGl = gt[3 * kC];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      f32x4_t acc = st[i] * eGl;
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) acc = Ch::step(tileA(kq + Gm::KTA * 64, i * KSC + ks), bUt[ks], acc);
+      st[i] = acc;
+    }
+  };
+
+  // O of chunk ci (tokens seq_start + 64 ci + 16 mt + 4 g + i, column 16 dvt + col)
+  const size_t rowstride = static_cast<size_t>(Hv) * D;
+  auto store_o = [&](int ci, const f32x4_t (&O)[4]) {
+    const int clen = min(kC, len - kC * ci);
+    E* ob = static_cast<E*>(A.o) + (static_cast<size_t>(seq_start + kC * ci + 4 * g)) * rowstride + h * D + 16 * dvt + col;
+    if (clen == kC) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * mt + 4 * g + i < clen) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
+    }
+  };
+
+  if (nc > 0) {
+    f32x4_t O[4];
+    stage(first, lds0);
+    wait_stage();
+    for (int ci = 0; ci < nc; ci += 2) {
+      if (Sm::NBUF == 2) {
+        if (ci + 1 < nc) stage(first + ci + 1, lds1);
+        if (ci > 0) store_o(ci - 1, O);
+        compute(lds0, O);
+        wait_stage();
+        if (ci + 1 < nc) {
+          if (ci + 2 < nc) stage(first + ci + 2, lds0);
+          store_o(ci, O);
+          compute(lds1, O);
+          wait_stage();
+        }
+      } else {
+        if (ci > 0) store_o(ci - 1, O);
+        compute(lds0, O);
+        if (ci + 1 < nc) {
+          lds_barrier();
+          stage(first + ci + 1, lds0);
+          wait_stage();
+          store_o(ci, O);
+          compute(lds0, O);
+          if (ci + 2 < nc) {
+            lds_barrier();
+            stage(first + ci + 2, lds0);
+            wait_stage();
+          }
         }
       }
     }
-
-    // step 5: S <- e^{G_last} S + Ut^T K
-    const float eGl = expf(g_l[buf][kC - 1]);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int tt = wave + 4 * i;
-      if (tt < NDT * NKT) {
-        const int dvt = tt / NKT, dkt = tt % NKT;
-        f32x4_t acc = Sacc[i] * eGl;
-#pragma unroll
-        for (int k0 = 0; k0 < kC; k0 += M::KSTEP)
-          acc = M::mma(op_at<BF16>(Ut_l, TLD, dvt * 16, k0, lane), op_at<BF16>(KTc, kC, dkt * 16, k0, lane), acc);
-        Sacc[i] = acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          S_l[(dvt * 16 + (lane >> 4) * 4 + e) * SLD + dkt * 16 + (lane & 15)] = M::cvt(acc[e]);
-      }
-    }
+    store_o(nc - 1, O);
   }
 
   // ---- final state back to the slot ----
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int tt = wave + 4 * i;
-    if (tt < NDT * NKT) {
-      const int dvt = tt / NKT, dkt = tt % NKT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dv = dvt * 16 + (lane >> 4) * 4 + e, dk = dkt * 16 + (lane & 15);
-        Sglob[static_cast<size_t>(dv0 + dv) * D + dk] = Sacc[i][e];
-      }
-    }
-  }
+  for (int i = 0; i < NT; ++i)
+    *reinterpret_cast<float4*>(Sglob + 16 * i + 4 * g) = make_float4(st[i][0], st[i][1], st[i][2], st[i][3]);
 
   // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
   if (A.W > 0) {
@@ -606,10 +908,9 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs A, PrefillLayout
       }
     };
     if (h % G == 0 && blockIdx.z == 0)
-      for (int cc = tid; cc < 2 * D; cc += blockDim.x) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
-    for (int cc = tid; cc < DVT; cc += blockDim.x) put(2 * Hk * D + h * D + dv0 + cc);
-    if (h == 0 && blockIdx.z == 0 && tid == 0)
-      A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
+      for (int cc = tid; cc < 2 * D; cc += CW * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
+    if (lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
+    if (h == 0 && blockIdx.z == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
   }
 }
 
@@ -618,21 +919,21 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs A, PrefillLayout
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 static int launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  const PrefillLayout L = prefill_layout(a.Hk, a.Hv, D, BF16, a.max_chunks, a.n_seqs);
+  constexpr int CW = Geo<D, BF16>::NT < 4 ? Geo<D, BF16>::NT : 4;
+  const PrefillLayout L = layout_t<D, BF16>(a.Hk, a.Hv, a.max_chunks, a.n_seqs);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a, L);
   int e = static_cast<int>(hipGetLastError());
   if (e) return e;
-  const size_t smem = ChunkSmem<D>::BYTES;
+  const size_t smem = ChunkSmem<D, BF16>::BYTES;
   e = static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<D, BF16>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(smem)));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
   if (e) return e;
   if (a.max_chunks > 0) {
-    hipLaunchKernelGGL((chunk_kernel<D, BF16>), dim3(a.max_chunks, a.Hk), dim3(256), smem, st, a, L);
+    hipLaunchKernelGGL((chunk_kernel<D, BF16>), dim3(a.max_chunks, a.Hk), dim3(kChunkThreads), smem, st, a, L);
     e = static_cast<int>(hipGetLastError());
     if (e) return e;
   }
-  hipLaunchKernelGGL((state_kernel<D, BF16>), dim3(a.n_seqs, a.Hv, D / StateShape<D>::DVT), dim3(256), 0,
+  hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(a.n_seqs, a.Hv, Geo<D, BF16>::NT / CW), dim3(CW * 64), 0,
                      st, a, L);
   return static_cast<int>(hipGetLastError());
 }

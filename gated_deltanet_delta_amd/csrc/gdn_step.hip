@@ -54,30 +54,61 @@ __device__ __forceinline__ float window_in1(const float* ring, uint32_t pos, int
 }
 
 // Causal depthwise conv (taps oldest first, tap W-1 on token j) + SiLU for
-// channels c..c+3.  W == 0 passes the input through.
-template <bool BF16>
+// channels c..c+3.  W is a compile-time constant so that every tap's loads are
+// issued together; W == 0 passes the input through.
+template <bool BF16, int W>
 __device__ __forceinline__ float4 conv4(const float* ring, uint32_t pos, int R, const void* xb,
-                                        int C, const float* w, int W, int j, int c) {
-  if (W == 0) return load_in4<BF16>(xb, static_cast<size_t>(j) * C + c);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int t = 0; t < W; ++t) {
-    const float4 in = window_in4<BF16>(ring, pos, R, xb, C, j - (W - 1) + t, c);
-    acc.x = fmaf(w[(c + 0) * W + t], in.x, acc.x);
-    acc.y = fmaf(w[(c + 1) * W + t], in.y, acc.y);
-    acc.z = fmaf(w[(c + 2) * W + t], in.z, acc.z);
-    acc.w = fmaf(w[(c + 3) * W + t], in.w, acc.w);
+                                        int C, const float* w, int j, int c) {
+  if constexpr (W == 0) {
+    return load_in4<BF16>(xb, static_cast<size_t>(j) * C + c);
+  } else {
+    float4 in[W];
+    float wt[4][W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) in[t] = window_in4<BF16>(ring, pos, R, xb, C, j - (W - 1) + t, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (W == 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(w + (c + i) * 4);
+        wt[i][0] = w4.x; wt[i][1] = w4.y; wt[i][2] = w4.z; wt[i][3] = w4.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < W; ++t) wt[i][t] = w[(c + i) * W + t];
+      }
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+      acc.x = fmaf(wt[0][t], in[t].x, acc.x);
+      acc.y = fmaf(wt[1][t], in[t].y, acc.y);
+      acc.z = fmaf(wt[2][t], in[t].z, acc.z);
+      acc.w = fmaf(wt[3][t], in[t].w, acc.w);
+    }
+    return make_float4(silu_f(acc.x), silu_f(acc.y), silu_f(acc.z), silu_f(acc.w));
   }
-  return make_float4(silu_f(acc.x), silu_f(acc.y), silu_f(acc.z), silu_f(acc.w));
 }
 
-template <bool BF16>
+template <bool BF16, int W>
 __device__ __forceinline__ float conv1(const float* ring, uint32_t pos, int R, const void* xb,
-                                       int C, const float* w, int W, int j, int c) {
-  if (W == 0) return load_in<BF16>(xb, static_cast<size_t>(j) * C + c);
-  float acc = 0.f;
-  for (int t = 0; t < W; ++t)
-    acc = fmaf(w[c * W + t], window_in1<BF16>(ring, pos, R, xb, C, j - (W - 1) + t, c), acc);
-  return silu_f(acc);
+                                       int C, const float* w, int j, int c) {
+  if constexpr (W == 0) {
+    return load_in<BF16>(xb, static_cast<size_t>(j) * C + c);
+  } else {
+    float in[W], wt[W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) in[t] = window_in1<BF16>(ring, pos, R, xb, C, j - (W - 1) + t, c);
+    if constexpr (W == 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(w + c * 4);
+      wt[0] = w4.x; wt[1] = w4.y; wt[2] = w4.z; wt[3] = w4.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < W; ++t) wt[t] = w[c * W + t];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < W; ++t) acc = fmaf(wt[t], in[t], acc);
+    return silu_f(acc);
+  }
 }
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
@@ -96,7 +127,7 @@ __device__ __forceinline__ float dot4v(f32x4_t a, float4 b) {
 
 // Decode (VERIFY = false: k = 1, state updated in place, position advanced)
 // and verify (VERIFY = true: k drafts, snapshot after each, state untouched).
-template <int D, bool BF16, bool VERIFY>
+template <int D, bool BF16, bool VERIFY, int W>
 __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A) {
   using Sh = StepShape<D>;
   constexpr int LPR = Sh::LPR;
@@ -124,9 +155,9 @@ __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A)
   for (int p = 0; p < NP; ++p)
     S[p] = load4(Sg + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4);
 
-  const int W = A.W, R = A.R, C = A.C;
-  const float* ring = A.W > 0 ? A.conv_state + static_cast<size_t>(slot) * R * C : nullptr;
-  const uint32_t pos = A.W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0u;
+  const int R = A.R, C = A.C;
+  const float* ring = W > 0 ? A.conv_state + static_cast<size_t>(slot) * R * C : nullptr;
+  const uint32_t pos = W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0u;
   const int kdr = VERIFY ? A.k : 1;
   const void* xb = static_cast<const char*>(A.x) +
                    static_cast<size_t>(b) * kdr * C * (BF16 ? 2 : 4);
@@ -138,8 +169,8 @@ __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A)
 
   for (int j = 0; j < kdr; ++j) {
     // ---- front end: conv + SiLU, L2 norm of q and k, gates ----
-    float4 q = conv4<BF16>(ring, pos, R, xb, C, A.conv_w, W, j, cq);
-    float4 k = conv4<BF16>(ring, pos, R, xb, C, A.conv_w, W, j, ck);
+    float4 q = conv4<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, cq);
+    float4 k = conv4<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, ck);
     float qs = A.q_scale, ks = 1.0f;
     if (A.flags & GDN_FLAG_L2NORM_QK) {
       const float sqq = group_sum<LPR>(dot4(q, q));
@@ -153,13 +184,13 @@ __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A)
     float v[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      v[p] = conv1<BF16>(ring, pos, R, xb, C, A.conv_w, W, j, cv0 + row0 + p * Sh::RPW);
+      v[p] = conv1<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, cv0 + row0 + p * Sh::RPW);
     const size_t gi = (static_cast<size_t>(b) * kdr + j) * A.Hv + h;
     const float alpha = expf(-softplus_f(load_in<BF16>(A.a, gi)));
     const float beta = sigmoid_f(load_in<BF16>(A.b, gi));
 
     // ---- append this token's raw input to the ring (rows nobody reads now) ----
-    if (W > 0) {
+    if constexpr (W > 0) {
       float* rrow = A.conv_state + (static_cast<size_t>(slot) * R + ring_row(pos + j, R)) * C;
       if (qk_writer) {
         *reinterpret_cast<float4*>(rrow + cq) = load_in4<BF16>(xb, static_cast<size_t>(j) * C + cq);
@@ -201,7 +232,7 @@ __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A)
 #pragma unroll
     for (int p = 0; p < NP; ++p)
       store_nt4(Sw + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4, S[p]);
-    if (W > 0) {
+    if constexpr (W > 0) {
       // Advance the position by this workgroup's share of one token; the
       // shares of the slot's workgroups sum to exactly 1 << kPosShift, and
       // no partial sum reaches it, so every reader of this call sees pos.
@@ -217,7 +248,7 @@ __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A)
 }
 
 // Standalone conv-ring step over all C channels: y = SiLU(conv), append x.
-template <bool BF16>
+template <bool BF16, int W>
 __global__ __launch_bounds__(256) void conv_step_kernel(StepArgs A) {
   const int b = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -226,12 +257,12 @@ __global__ __launch_bounds__(256) void conv_step_kernel(StepArgs A) {
     if (threadIdx.x == 0 && blockIdx.x == 0) report_error(A.dev_err, GDN_DEV_BAD_SLOT);
     return;
   }
-  const int C = A.C, R = A.R, W = A.W;
+  const int C = A.C, R = A.R;
   const float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
   const uint32_t pos = static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift;
   const void* xb = static_cast<const char*>(A.x) + static_cast<size_t>(b) * C * (BF16 ? 2 : 4);
   if (c < C) {
-    const float y = conv1<BF16>(ring, pos, R, xb, C, A.conv_w, W, 0, c);
+    const float y = conv1<BF16, W>(ring, pos, R, xb, C, A.conv_w, 0, c);
     store_out<BF16>(A.o, static_cast<size_t>(b) * C + c, y);
     A.conv_state[(static_cast<size_t>(slot) * R + ring_row(pos, R)) * C + c] = load_in<BF16>(xb, c);
   }
@@ -281,7 +312,9 @@ template <int D, bool BF16, bool VERIFY>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
   using Sh = StepShape<D>;
   dim3 grid(a.Hv * Sh::WG_PER_HEAD, a.batch);
-  hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY>), grid, dim3(Sh::THREADS), 0, s, a);
+  if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4>), grid, dim3(Sh::THREADS), 0, s, a);
+  else if (a.W == 0) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 0>), grid, dim3(Sh::THREADS), 0, s, a);
+  else return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -303,8 +336,9 @@ int launch_verify(const StepArgs& a, bool bf16, void* stream) { return launch_st
 int launch_conv_step(const StepArgs& a, bool bf16, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid((a.C + 255) / 256, a.batch);
-  if (bf16) hipLaunchKernelGGL(conv_step_kernel<true>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(conv_step_kernel<false>, grid, dim3(256), 0, s, a);
+  if (a.W != 4) return static_cast<int>(hipErrorInvalidValue);
+  if (bf16) hipLaunchKernelGGL((conv_step_kernel<true, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((conv_step_kernel<false, 4>), grid, dim3(256), 0, s, a);
   return static_cast<int>(hipGetLastError());
 }
 
