@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # MFMA accumulators in VGPRs: the chained products feed them straight to VALU
+    # code and the next MFMA, so AGPR<->VGPR copies would only add instructions
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 

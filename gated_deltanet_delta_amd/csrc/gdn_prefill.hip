@@ -718,25 +718,25 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
   // arrays, so loads landing in one never make the compiler wait before
   // reading the other.
   const char* wsb = static_cast<const char*>(A.workspace);
+  // Every 1 KB block of the buffer lies in one segment (the segment sizes are
+  // multiples of 1 KB), so the source base is wave-uniform and each lane adds
+  // its 16-byte offset.
+  static_assert(Sm::KQ % 1024 == 0 && Sm::TP % 1024 == 0 && Sm::VC % 512 == 0, "segment alignment");
   auto stage = [&](int chunk, char* base) {
     const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
     const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
     const char* vcb = hb + Gm::VC_OFF + static_cast<size_t>(blockIdx.z) * CW * 4 * P::VC_BYTES;
-    constexpr int NBLK = static_cast<int>((Sm::BUF + 1023) / 1024);
-#pragma unroll
-    for (int j = 0; j < (NBLK + CW - 1) / CW; ++j) {
-      const int b = wave + j * CW;                  // 1 KB block of the buffer
-      if (b < NBLK) {
-        const int u = b * 64 + lane;                // 16-byte unit
-        const char* src = u < U_KQ ? kq + 16 * u
-                        : u < U_TP ? hb + 16 * (u - U_KQ)
-                        : u < U_VC ? vcb + 16 * (u - U_TP)
-                                   : hb + Gm::GATE_OFF + 16 * (u - U_VC);
-        if (u < Sm::UNITS)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src),
-                                           (__attribute__((address_space(3))) void*)(base + b * 1024), 16, 0, 0);
-      }
-    }
+    constexpr int NKQ = static_cast<int>(Sm::KQ / 1024), NTP = static_cast<int>(Sm::TP / 1024);
+    auto dma = [&](const char* src, char* dst, int lim) {
+      if (lane * 16 < lim)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src) + lane,
+                                         (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+    };
+    for (int b = wave; b < NKQ; b += CW) dma(kq + b * 1024, base + b * 1024, 1024);
+    for (int b = wave; b < NTP; b += CW) dma(hb + b * 1024, base + Sm::KQ + b * 1024, 1024);
+    for (int b = wave; b * 1024 < static_cast<int>(Sm::VC); b += CW)
+      dma(vcb + b * 1024, base + Sm::KQ + Sm::TP + b * 1024, static_cast<int>(Sm::VC) - b * 1024);
+    if (wave == CW - 1) dma(hb + Gm::GATE_OFF, base + Sm::KQ + Sm::TP + Sm::VC, static_cast<int>(Sm::GATES));
   };
   auto wait_stage = [&]() {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 static int launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  constexpr int CW = Geo<D, BF16>::NT < 4 ? Geo<D, BF16>::NT : 4;
+  constexpr int CW = Geo<D, BF16>::NT < 2 ? Geo<D, BF16>::NT : 2;
   const PrefillLayout L = layout_t<D, BF16>(a.Hk, a.Hv, a.max_chunks, a.n_seqs);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a, L);
   int e = static_cast<int>(hipGetLastError());
