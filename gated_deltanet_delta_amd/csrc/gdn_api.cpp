@@ -312,6 +312,9 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
   if (s != GDN_OK) return s;
   if (chunk != gdn::kChunk)
     return fail(GDN_ERR_UNSUPPORTED, "chunk: %d, required in this build: %d", chunk, gdn::kChunk);
+  if (g->dtype_in == GDN_F32 && g->d_k > 64)
+    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d with dtype_in GDN_F32, required for prefill in this build: <= 64",
+                g->d_k);
   if (n_seqs < 1 || n_seqs > g->n_slots)
     return fail(GDN_ERR_RANGE, "n_seqs: %d, required: 1..n_slots = %d", n_seqs, g->n_slots);
   if (n_tokens < 0) return fail(GDN_ERR_RANGE, "n_tokens: %d, required: >= 0", n_tokens);

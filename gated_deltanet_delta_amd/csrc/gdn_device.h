@@ -10,6 +10,7 @@ constexpr int kWave = 64;
 constexpr int kPosShift = 16;  // conv_pos counts tokens in units of 1/65536
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -22,6 +23,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
 // Round to nearest even (the hardware v_cvt_pk_bf16_f32 of gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two values rounded to bf16 and packed (lo in bits 0-15): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two input/output dtypes: BF16 = true reads bf16 bits.

@@ -47,11 +47,12 @@ struct PrefillArgs {
   int32_t Hk, Hv, D, C, W, R, n_slots;
   uint32_t flags;
   float q_scale, l2_eps;
+  int32_t seg_lo, seg_hi;  // chunk-table range of one launch segment (set by the launcher)
 };
 
 // Byte offsets and block sizes of the prefill workspace.
-//   kq:   per (chunk, k-head) block of packed K, Q and K^T operands (kq_bytes each)
-//   head: per (chunk, v-head) block of packed T, P, V and the gates (head_bytes each)
+//   kq:   per (chunk, k-head) block of packed Q operand tiles (kq_bytes each)
+//   head: per (chunk, v-head) block of packed -W, decayed K^T, P, U', the gate factors and V (head_bytes each)
 struct PrefillLayout {
   size_t kq, head, chunk_tab, seq_tab, counters, total;
   size_t kq_bytes, head_bytes;

@@ -4,9 +4,10 @@
 // G_r = sum_{j<=r} g_j and the state S at the chunk start (d_v x d_k):
 //   L_rj = beta_r e^{G_r - G_j} (k_r . k_j)   for r > j (0 otherwise)
 //   T    = (I + L)^{-1}                                      (unit lower triangular)
-//   U    = T diag(beta) (V - diag(e^G) K S^T)               (the corrected writes u_r)
+//   W    = T diag(beta e^G) K,   U' = T diag(beta) V        (chunk-local)
+//   U    = U' - W S^T                                        (the corrected writes u_r)
 //   O    = diag(e^G) Q S^T + P U,  P_rj = e^{G_r - G_j} (q_r . k_j) for j <= r
-//   S   <- e^{G_last} S + (diag(e^{G_last - G}) U)^T K
+//   S   <- e^{G_last} S + U^T diag(e^{G_last - G}) K
 // This is an exact reorganisation of the token-by-token rule (it follows from
 // unrolling S_r = alpha_r S_{r-1} + u_r k_r^T inside the chunk).  Every
 // exponent is a difference G_r - G_j with r >= j (or G_r itself), so it is
@@ -18,19 +19,20 @@
 //           partial) and validates slots and lengths -- no host sync;
 //   chunk:  one workgroup per (chunk, k-head), all chunks in parallel: conv +
 //           SiLU + L2 norm of the chunk's q, k and v, gates and their
-//           cumulative sums, K K^T and Q K^T on MFMA, then per v-head L, the
-//           inverse T and P.  Every matrix the next kernel multiplies is
-//           written pre-packed in MFMA operand order (below), V already
-//           scaled by beta, and the per-token gate factors precomputed;
+//           cumulative sums, K K^T and K Q^T on MFMA, then per v-head P, the
+//           inverse T, W and U'.  Everything the next kernel multiplies is
+//           written pre-packed in MFMA operand order (below);
 //   chain:  one wave per (sequence, v-head, 16 rows of d_v) walks the
 //           sequence's chunks in order.  It keeps its 16 x d_k slice of the
 //           state, transposed, in MFMA accumulators and never leaves
 //           registers: every product's result feeds the next product as its
 //           B operand directly (the contraction order inside an MFMA is a
 //           free permutation, so the A operand is packed in the permuted
-//           order that matches the accumulator layout).  The waves of a
-//           workgroup share the chunk's packed operands, staged into LDS
-//           with direct global->LDS loads one chunk ahead.
+//           order that matches the accumulator layout).  Per chunk it does
+//           only what depends on the state: U = U' - W S^T, Q S^T, P U and
+//           the state update.  The waves of a workgroup share the chunk's
+//           packed operands, staged into LDS with direct global->LDS loads
+//           one chunk ahead.
 //
 // Packed operand tiles.  A 16 x SK sub-matrix (rows r, contraction index k;
 // SK = 32 for the bf16 MFMA 16x16x32, 16 for four fp32 MFMA 16x16x4) is
@@ -38,11 +40,16 @@
 // element e = (k / 16) * 4 + k % 4, the value at (r, k).  A 16x16
 // accumulator tile holds rows 4g..4g+3 of column l%16 in lane l, so the
 // accumulators of tiles (2s, 2s+1) (bf16) or tile s (fp32) form exactly the
-// B operand that pairs with packed tile column s.
+// B operand that pairs with packed tile column s -- and, read the other way,
+// the packed A tile of the transposed product.
 #include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+
+#ifndef GDN_CHAIN_SCHED
+#define GDN_CHAIN_SCHED 1
+#endif
 
 namespace gdn {
 
@@ -67,18 +74,19 @@ struct Geo {
   static constexpr int KSD = (D + P::SK - 1) / P::SK;  // packed tiles along d
   static constexpr int KSC = kC / P::SK;               // packed tiles along the chunk
   static constexpr int NT = D / 16;                    // 16-row tiles along d
-  static constexpr int KA = 0;                         // K  as A (rows tok, k = d):   4 x KSD
-  static constexpr int QA = 4 * KSD;                   // Q  as A:                     4 x KSD
-  static constexpr int KTA = 8 * KSD;                  // K^T as A (rows d, k = tok): NT x KSC
-  static constexpr int KQ_TILES = 8 * KSD + NT * KSC;
-  static constexpr int TA = 0;                         // T as A (rows r, k = j):      4 x KSC
-  static constexpr int PA = 4 * KSC;                   // P as A:                      4 x KSC
-  static constexpr size_t VC_OFF = 8 * KSC * kTileBytes;            // V, accumulator layout [NT][4]
-  // per-token factors: e^G, beta e^G, e^{G_last - G}, then e^{G_last} (4 x 64 floats)
-  static constexpr size_t GATE_OFF = VC_OFF + NT * 4 * P::VC_BYTES;
-  static constexpr size_t GATE_BYTES = 4 * kC * 4;
-  static constexpr size_t KQ_BYTES = KQ_TILES * kTileBytes;
-  static constexpr size_t HEAD_BYTES = GATE_OFF + GATE_BYTES;
+  static constexpr int TPS = P::SK / 16;               // accumulator tiles per packed super-step
+  // per (chunk, k-head): Q as A (rows token, k = d), 4 x KSD tiles
+  static constexpr size_t KQ_BYTES = 4 * KSD * kTileBytes;
+  // per (chunk, v-head), in this order:
+  static constexpr int WA = 0;                 // -W as A (rows token, k = d):                     4 x KSD
+  static constexpr int KDA = 4 * KSD;          // (diag(e^{G_last - G}) K)^T as A (rows d, k = tok): NT x KSC
+  static constexpr int PA = KDA + NT * KSC;    // P as A (rows r, k = j):                           4 x KSC
+  static constexpr int HT_TILES = PA + 4 * KSC;
+  static constexpr size_t VW_OFF = HT_TILES * kTileBytes;           // U', accumulator layout [NT][4]
+  static constexpr size_t GATE_OFF = VW_OFF + NT * 4 * P::VC_BYTES;  // e^G (64 floats), e^{G_last} (64 copies)
+  static constexpr size_t GATE_BYTES = 2 * kC * 4;
+  static constexpr size_t VB_OFF = GATE_OFF + GATE_BYTES;            // V, accumulator layout [NT][4] (chunk kernel)
+  static constexpr size_t HEAD_BYTES = VB_OFF + NT * 4 * P::VC_BYTES;
 };
 
 int prefill_max_chunks(int n_tokens, int n_seqs) { return (n_tokens + kC - 1) / kC + n_seqs; }
@@ -335,41 +343,83 @@ __device__ __forceinline__ uint4 pack_lane(F f) {
 }
 
 // ---------------------------------------------------------------------------
-// chunk: front end, gates, K K^T / Q K^T, inverse T, P  (8 waves)
+// chunk: front end, gates, K K^T / K Q^T, then per v-head P, T, W and U'
+// (8 waves)
 // ---------------------------------------------------------------------------
-constexpr int kChunkThreads = 512;
+constexpr int kChunkThreads = 640;  // 10 waves: one conv item per thread at G = 3, d = 128
+constexpr int kChunkWaves = kChunkThreads / 64;
 
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// LDS of the chunk kernel, by lifetime:
+//   R0: conv outputs of q | k (fp32), then L -> T and inverse scratch of NH heads
+//   R1: k (hi, lo for bf16) and q as A tiles, then T diag(beta e^G), T diag(beta) of NH heads
+//   KT: K^T as A tiles;  AM: K K^T;  MISC: per-token gate tables and norm factors
 template <int D, bool BF16>
 struct ChunkSmem {
-  static constexpr int QK_LD = 2 * D + 1;               // q in [0,D), k in [D,2D)
-  static constexpr int QK = (kC * QK_LD > 4 * kC * kLd) ? kC * QK_LD : 4 * kC * kLd;  // qk, then L/T
-  static constexpr int PKT = BF16 ? 3 * 4 * Geo<D, BF16>::KSD * kTileBytes / 4 : 0;   // hi, lo, q tiles
-  static constexpr int PK = PKT > 4 * 32 * 33 ? PKT : 4 * 32 * 33;                   // then inverse scratch
-  static constexpr int AB = 2 * kC * kLd;
-  static constexpr int MISC = 2 * kMaxGroup * kC + 2 * kC;
-  static constexpr size_t BYTES = static_cast<size_t>(QK + PK + AB + MISC) * 4;
+  using Gm = Geo<D, BF16>;
+  static constexpr int NH = BF16 ? 3 : 1;            // v-heads per inverse group
+  static constexpr int QK_LD = 2 * D + 4;            // rows 16-byte aligned
+  static constexpr int PK_Q = BF16 ? 2 : 1;          // index of the q tiles in R1
+  static constexpr size_t LT1 = static_cast<size_t>(kC) * kLd * 4;
+  static constexpr size_t SCR1 = 32 * 33 * 4;
+  static constexpr size_t R0 = cmax(static_cast<size_t>(kC) * QK_LD * 4, NH * (LT1 + SCR1));
+  static constexpr size_t TT1 = 2 * 4 * Gm::KSC * kTileBytes;
+  static constexpr size_t R1 = cmax((PK_Q + 1) * 4 * Gm::KSD * kTileBytes, NH * TT1);
+  static constexpr size_t KT = static_cast<size_t>(Gm::NT) * Gm::KSC * kTileBytes;
+  static constexpr size_t AM = LT1;
+  static constexpr size_t MISC = static_cast<size_t>(4 * kMaxGroup * kC + 2 * kC) * 4;
+  static constexpr size_t BYTES = R0 + R1 + KT + AM + MISC;
 };
 
-template <int D, bool BF16>
+// The chunk tile list of the P products: (row tile ti, packed column ks) with
+// ks * SK <= 16 ti + 15, i.e. the tiles of a lower-triangular 64x64 matrix
+// that are not identically zero.
+template <bool BF16>
+struct TriTiles {
+  static constexpr int SK = Pk<BF16>::SK;
+  static constexpr int count() {
+    int n = 0;
+    for (int ti = 0; ti < 4; ++ti) n += (16 * ti + 15) / SK + 1;
+    return n;
+  }
+  __device__ static void at(int t, int& ti, int& ks) {
+    ti = 0;
+    while (t > (16 * ti + 15) / SK) { t -= (16 * ti + 15) / SK + 1; ++ti; }
+    ks = t;
+  }
+};
+
+// KW: conv width, 4 or 0 (inputs are q | k | v directly); a compile-time
+// constant so the unrolled per-token conv code has no branches.
+template <int D, bool BF16, int KW>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, PrefillLayout Lay) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ChunkSmem<D, BF16>;
+  using Ch = Chain<BF16>;
+  using Bop = typename Ch::Bop;
   using E = typename P::E;
-  constexpr int VE = 16 / sizeof(E);            // channels per 16-byte input vector
-  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT;
+  constexpr int VE = 4;                          // channels per conv item (one 8- or 16-byte load per row)
+  using RawT = typename std::conditional<BF16, uint2, uint4>::type;
+  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT, TPS = Gm::TPS, SK = P::SK, EPL = P::EPL;
+  constexpr int NH = Sm::NH, QK_LD = Sm::QK_LD;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* qk = smem;                               // [64][2D+1] raw conv outputs of q | k
-  float* Lt = smem;                               // [4][64][65] L -> T   (per-head phase)
-  uint4* pk = reinterpret_cast<uint4*>(smem + Sm::QK);  // packed k_hi, k_lo, q tiles (bf16 only)
-  float* tmpw = smem + Sm::QK;                    // [4][32][33] inverse scratch (per-head phase)
-  float* Am = smem + Sm::QK + Sm::PK;             // [64][65] K K^T (normalised)
-  float* Bm = Am + kC * kLd;                      // [64][65] Q K^T (normalised, q_scale)
-  float* gcum = Bm + kC * kLd;                    // [8][64]
-  float* bet = gcum + kMaxGroup * kC;             // [8][64]
-  float* inv = bet + kMaxGroup * kC;              // [2][64]  q and k scale factors
+  char* sb = reinterpret_cast<char*>(smem);
+  float* qk = smem;                                        // [64][QK_LD] conv outputs of q | k
+  float* Lt = smem;                                        // NH x [64][65]: L -> T
+  float* tmpw = smem + NH * kC * kLd;                      // NH x [32][33] inverse scratch
+  uint4* pk = reinterpret_cast<uint4*>(sb + Sm::R0);       // k (hi, lo) and q as A tiles
+  uint4* tt = pk;                                          // NH x 2 x [4 x KSC] T tiles
+  uint4* kt = reinterpret_cast<uint4*>(sb + Sm::R0 + Sm::R1);  // K^T as A: NT x KSC tiles
+  float* Am = reinterpret_cast<float*>(sb + Sm::R0 + Sm::R1 + Sm::KT);  // [64][65] K K^T
+  float* gcum = Am + kC * kLd;                             // [8][64] G
+  float* bet = gcum + kMaxGroup * kC;                      // [8][64] beta
+  float* dkf = bet + kMaxGroup * kC;                       // [8][64] e^{G_last - G}
+  float* bge = dkf + kMaxGroup * kC;                       // [8][64] beta e^G
+  float* inv = bge + kMaxGroup * kC;                       // [2][64] q and k norm factors
 
-  const int chunk = blockIdx.x;
+  const int chunk = A.seg_lo + blockIdx.x;
   const int kh = blockIdx.y;
   const int n_chunks = ws_ptr<int32_t>(A.workspace, Lay.counters)[0];
   if (chunk >= n_chunks) return;
@@ -380,9 +430,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
   const int slot = se[SQ_SLOT];
   const int seq_start = se[SQ_START];
-  const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, C = A.C, R = A.R, W = A.W;
+  const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, C = A.C, R = A.R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int NCH = (2 + G) * D;                    // channels of this k-head: q | k | v of its v-heads
   const E* x = static_cast<const E*>(A.x);
   char* kqb = static_cast<char*>(A.workspace) + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
   auto headb = [&](int h) {
@@ -392,8 +441,125 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     return cc < D ? kh * D + cc : (cc < 2 * D ? Hk * D + kh * D + (cc - D) : 2 * Hk * D + kh * G * D + (cc - 2 * D));
   };
 
-  // ---- gates: one wave per v-head, lane = token, fixed-order inclusive scan ----
-  for (int hi = wave; hi < G; hi += kChunkThreads / 64) {
+  // ---- conv + SiLU: item = (VE channels, 16 tokens), the 19-row window in registers.
+  // q|k items first, then v items; each wave takes a contiguous run of items. ----
+  {
+    const int nvq = 2 * D / VE, nvv = G * D / VE;
+    const int n_items = 4 * (nvq + nvv);
+    const int ipw = (n_items + kChunkWaves - 1) / kChunkWaves;
+    for (int jj = lane; jj < ipw; jj += 64) {
+      const int item = wave * ipw + jj;
+      if (item >= n_items) break;
+      int q, vec;
+      if (item < 4 * nvq) {
+        q = item / nvq;
+        vec = item - q * nvq;
+      } else {
+        const int i2 = item - 4 * nvq;
+        q = i2 / nvv;
+        vec = nvq + (i2 - q * nvv);
+      }
+      const int cc0 = vec * VE;
+      const int c0 = xchan(cc0);
+      const int tq = 16 * q;                        // first token of this quarter
+      // raw rows: tokens t0+tq-3 .. t0+tq+15 (row i <-> token t0+tq-3+i),
+      // clamped into the sequence and the chunk so every load is valid
+      RawT raw[19];
+#pragma unroll
+      for (int i = 0; i < 19; ++i) {
+        const int t = min(max(t0 + tq - 3 + i, seq_start), t0 + len - 1);
+        raw[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
+      }
+      float w[VE][4];
+      if constexpr (KW == 4) {
+#pragma unroll
+        for (int v = 0; v < VE; ++v) {
+          const float4 w4 = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
+          w[v][0] = w4.x; w[v][1] = w4.y; w[v][2] = w4.z; w[v][3] = w4.w;
+        }
+      }
+      auto elem = [&](const RawT& r, int v) -> float {
+        if constexpr (BF16) {
+          const uint32_t wv = v < 2 ? r.x : r.y;
+          return __uint_as_float((v & 1) ? (wv & 0xffff0000u) : (wv << 16));
+        } else {
+          return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
+        }
+      };
+      // the three rows before the quarter: x, or the ring / zero before the sequence
+      float hist[VE][3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int t = t0 + tq - 3 + i;
+#pragma unroll
+        for (int v = 0; v < VE; ++v) hist[v][i] = elem(raw[i], v);
+        if (t < seq_start) {
+          if (init) {
+            const float* rr = A.conv_state + (static_cast<size_t>(slot) * R +
+                                              ring_row(pos0 + static_cast<uint32_t>(t - seq_start), R)) * C + c0;
+#pragma unroll
+            for (int v = 0; v < VE; ++v) hist[v][i] = rr[v];
+          } else {
+#pragma unroll
+            for (int v = 0; v < VE; ++v) hist[v][i] = 0.f;
+          }
+        }
+      }
+      const bool is_v = cc0 >= 2 * D;
+      const int hv = is_v ? (cc0 - 2 * D) / D : 0;  // v-head within the group
+      const int dv0 = is_v ? (cc0 - 2 * D) % D : 0;
+      E* vcb = reinterpret_cast<E*>(headb(kh * G + hv) + Gm::VB_OFF);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {              // 4 groups of 4 tokens
+        float y[VE][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;                 // token within the quarter
+          const bool valid = tq + r < len;
+#pragma unroll
+          for (int v = 0; v < VE; ++v) {
+            const float xin = elem(raw[3 + r], v);
+            float yy;
+            if constexpr (KW == 4) {
+              float acc = w[v][0] * hist[v][0];
+              acc = fmaf(w[v][1], hist[v][1], acc);
+              acc = fmaf(w[v][2], hist[v][2], acc);
+              acc = fmaf(w[v][3], xin, acc);
+              yy = silu_fast(acc);
+              hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
+            } else {
+              yy = xin;
+            }
+            y[v][i] = valid ? yy : 0.f;
+          }
+        }
+        if (!is_v) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* dst = qk + (tq + 4 * g4 + i) * QK_LD + cc0;
+#pragma unroll
+            for (int v = 0; v < VE; v += 4)
+              *reinterpret_cast<float4*>(dst + v) = make_float4(y[v][i], y[v + 1][i], y[v + 2][i], y[v + 3][i]);
+          }
+        } else {
+          // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i
+#pragma unroll
+          for (int v = 0; v < VE; ++v) {
+            const int dv = dv0 + v;
+            E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
+            if constexpr (BF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(y[v][0], y[v][1]), pack2_bf16(y[v][2], y[v][3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- gates: one wave per v-head (the last waves), lane = token, fixed-order inclusive scan ----
+  for (int hi = kChunkWaves - 1 - wave; hi >= 0 && hi < G; hi += kChunkWaves) {
     const int h = kh * G + hi;
     float g = 0.f, bb = 0.f;
     if (lane < len) {
@@ -406,290 +572,328 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       const float up = __shfl_up(g, off, 64);
       if (lane >= off) g += up;
     }
-    gcum[hi * kC + lane] = g;
-    bet[hi * kC + lane] = bb;
     const float glast = __shfl(g, 63, 64);
     const float eg = __expf(g);
+    gcum[hi * kC + lane] = g;
+    bet[hi * kC + lane] = bb;
+    dkf[hi * kC + lane] = __expf(glast - g);
+    bge[hi * kC + lane] = bb * eg;
     float* gw = reinterpret_cast<float*>(headb(h) + Gm::GATE_OFF);
     gw[lane] = eg;
-    gw[kC + lane] = bb * eg;
-    gw[2 * kC + lane] = __expf(glast - g);
-    gw[3 * kC + lane] = __expf(glast);
+    gw[kC + lane] = __expf(glast);
   }
 
-  __syncthreads();  // betas are in LDS: V is stored pre-scaled by beta
-
-  // ---- conv + SiLU: item = (VE channels, 16 tokens), the 19-row window in registers ----
-  const int nvec = NCH / VE;
-  for (int item = tid; item < 4 * nvec; item += kChunkThreads) {
-    const int q = item / nvec, cc0 = (item - q * nvec) * VE;
-    const int c0 = xchan(cc0);
-    const int tq = 16 * q;                        // first token of this quarter
-    // raw rows: tokens t0+tq-3 .. t0+tq+15 (row i <-> token t0+tq-3+i),
-    // clamped into the sequence and the chunk so every load is valid
-    uint4 raw[19];
-#pragma unroll
-    for (int i = 0; i < 19; ++i) {
-      const int t = min(max(t0 + tq - 3 + i, seq_start), t0 + len - 1);
-      raw[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * C + c0);
-    }
-    float w[VE][4];
-    if (W == 4) {
-#pragma unroll
-      for (int v = 0; v < VE; ++v) {
-        const float4 w4 = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
-        w[v][0] = w4.x; w[v][1] = w4.y; w[v][2] = w4.z; w[v][3] = w4.w;
-      }
-    }
-    auto elem = [&](const uint4& r, int v) -> float {
-      if constexpr (BF16) {
-        const uint32_t wv = (v >> 1) == 0 ? r.x : (v >> 1) == 1 ? r.y : (v >> 1) == 2 ? r.z : r.w;
-        return __uint_as_float((v & 1) ? (wv & 0xffff0000u) : (wv << 16));
-      } else {
-        return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
-      }
-    };
-    // the three rows before the quarter: x, or the ring / zero before the sequence
-    float hist[VE][3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int t = t0 + tq - 3 + i;
-#pragma unroll
-      for (int v = 0; v < VE; ++v) hist[v][i] = elem(raw[i], v);
-      if (t < seq_start) {
-        if (init) {
-          const float* rr = A.conv_state + (static_cast<size_t>(slot) * R +
-                                            ring_row(pos0 + static_cast<uint32_t>(t - seq_start), R)) * C + c0;
-#pragma unroll
-          for (int v = 0; v < VE; ++v) hist[v][i] = rr[v];
-        } else {
-#pragma unroll
-          for (int v = 0; v < VE; ++v) hist[v][i] = 0.f;
-        }
-      }
-    }
-    const bool is_v = cc0 >= 2 * D;
-    const int hv = is_v ? (cc0 - 2 * D) / D : 0;  // v-head within the group
-    const int dv0 = is_v ? (cc0 - 2 * D) % D : 0;
-    E* vcb = reinterpret_cast<E*>(headb(kh * G + hv) + Gm::VC_OFF);
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {              // 4 groups of 4 tokens
-      float y[VE][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i;                 // token within the quarter
-        const bool valid = tq + r < len;
-#pragma unroll
-        for (int v = 0; v < VE; ++v) {
-          const float xin = elem(raw[3 + r], v);
-          float yy;
-          if (W == 4) {
-            float acc = w[v][0] * hist[v][0];
-            acc = fmaf(w[v][1], hist[v][1], acc);
-            acc = fmaf(w[v][2], hist[v][2], acc);
-            acc = fmaf(w[v][3], xin, acc);
-            yy = silu_fast(acc);
-            hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
-          } else {
-            yy = xin;
-          }
-          y[v][i] = valid ? yy : 0.f;
-        }
-      }
-      if (!is_v) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int v = 0; v < VE; ++v) qk[(tq + 4 * g4 + i) * Sm::QK_LD + cc0 + v] = y[v][i];
-      } else {
-        // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i;
-        // stored as beta * v
-        const float4 bq = *reinterpret_cast<const float4*>(bet + hv * kC + tq + 4 * g4);
-#pragma unroll
-        for (int v = 0; v < VE; ++v) {
-          y[v][0] *= bq.x; y[v][1] *= bq.y; y[v][2] *= bq.z; y[v][3] *= bq.w;
-        }
-#pragma unroll
-        for (int v = 0; v < VE; ++v) {
-          const int dv = dv0 + v;
-          E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
-          if constexpr (BF16) {
-            uint2 pkd;
-            pkd.x = static_cast<uint32_t>(f32_to_bf16_bits(y[v][0])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[v][1])) << 16);
-            pkd.y = static_cast<uint32_t>(f32_to_bf16_bits(y[v][2])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[v][3])) << 16);
-            *reinterpret_cast<uint2*>(dst) = pkd;
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
-          }
-        }
-      }
-    }
-  }
   __syncthreads();
 
-  // ---- L2 norm factors of q and k per token (fixed reduction order) ----
-  const bool norm = (A.flags & GDN_FLAG_L2NORM_QK) != 0;
-  for (int r = wave * 8; r < wave * 8 + 8; ++r) {
+  // ---- L2 norm factors of q and k per token: 8 lanes per token, fixed order ----
+  {
+    const bool norm = (A.flags & GDN_FLAG_L2NORM_QK) != 0;
+    constexpr int PER = D / 8;
+    const int r = (wave & 7) * 8 + (lane >> 3), part = lane & 7;  // waves 0-7: 8 tokens each
+    const float* qr = qk + r * QK_LD + part * PER;
     float sq = 0.f, sk = 0.f;
-    for (int d = lane; d < D; d += 64) {
-      const float qv = qk[r * Sm::QK_LD + d];
-      const float kv = qk[r * Sm::QK_LD + D + d];
-      sq = fmaf(qv, qv, sq);
-      sk = fmaf(kv, kv, sk);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float a = qr[e], b = qr[D + e];
+      sq = fmaf(a, a, sq);
+      sk = fmaf(b, b, sk);
     }
-    sq = group_sum<64>(sq);
-    sk = group_sum<64>(sk);
-    if (lane == 0) {
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      sq += __shfl_xor(sq, off, 64);
+      sk += __shfl_xor(sk, off, 64);
+    }
+    if (part == 0 && wave < 8) {
       inv[r] = norm ? A.q_scale * (1.0f / sqrtf(sq + A.l2_eps)) : A.q_scale;
       inv[kC + r] = norm ? 1.0f / sqrtf(sk + A.l2_eps) : 1.0f;
     }
   }
   __syncthreads();
-  auto qn = [&](int r, int d) { return qk[r * Sm::QK_LD + d] * inv[r]; };
-  auto kn = [&](int r, int d) { return qk[r * Sm::QK_LD + D + d] * inv[kC + r]; };
+  auto qn = [&](int r, int d) { return qk[r * QK_LD + d] * inv[r]; };
+  auto kn = [&](int r, int d) { return qk[r * QK_LD + D + d] * inv[kC + r]; };
+  auto pack = [&](const float (&v)[EPL]) { return pack_lane<BF16>([&](int e) { return v[e]; }); };
 
-  // ---- packed K, Q (rows tok, k = d) and K^T (rows d, k = tok) to the workspace ----
-  // (bf16: also k_hi, k_lo, q tiles into LDS for the K K^T / Q K^T products)
+  // ---- packing: K (hi, lo) and Q as A tiles (rows token, k = d) into LDS, Q also
+  // to the workspace; K^T as A (rows d, k = token) into LDS; per v-head
+  // (diag(e^{G_last - G}) K)^T to the workspace ----
   for (int u = tid; u < 4 * KSD * 64; u += kChunkThreads) {
     const int tile = u >> 6, ln = u & 63;
     const int mt = tile / KSD, ks = tile % KSD;
     const int row = 16 * mt + (ln & 15), g = ln >> 4;
-    auto kof = [&](int e) { return ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3); };
-    const uint4 kw = pack_lane<BF16>([&](int e) { const int k = kof(e); return k < D ? kn(row, k) : 0.f; });
-    const uint4 qw = pack_lane<BF16>([&](int e) { const int k = kof(e); return k < D ? qn(row, k) : 0.f; });
-    reinterpret_cast<uint4*>(kqb + (Gm::KA + tile) * kTileBytes)[ln] = kw;
-    reinterpret_cast<uint4*>(kqb + (Gm::QA + tile) * kTileBytes)[ln] = qw;
+    float kv[EPL], qv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int k = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+      kv[e] = k < D ? kn(row, k) : 0.f;
+      qv[e] = k < D ? qn(row, k) : 0.f;
+    }
+    const uint4 qw = pack(qv);
+    reinterpret_cast<uint4*>(kqb)[tile * 64 + ln] = qw;
+    pk[(Sm::PK_Q * 4 * KSD + tile) * 64 + ln] = qw;
+    pk[tile * 64 + ln] = pack(kv);
     if constexpr (BF16) {
-      const uint4 lw = pack_lane<BF16>([&](int e) {
-        const int k = kof(e);
-        if (k >= D) return 0.f;
-        const float v = kn(row, k);
-        return v - bf16_bits_to_f32(f32_to_bf16_bits(v));
-      });
-      pk[(0 * 4 * KSD + tile) * 64 + ln] = kw;
-      pk[(1 * 4 * KSD + tile) * 64 + ln] = lw;
-      pk[(2 * 4 * KSD + tile) * 64 + ln] = qw;
+      float lo[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) lo[e] = kv[e] - bf16_bits_to_f32(f32_to_bf16_bits(kv[e]));
+      pk[(4 * KSD + tile) * 64 + ln] = pack(lo);
     }
   }
   for (int u = tid; u < NT * KSC * 64; u += kChunkThreads) {
     const int tile = u >> 6, ln = u & 63;
-    const int mt = tile / KSC, ks = tile % KSC;
-    const int dk = 16 * mt + (ln & 15), g = ln >> 4;
-    const uint4 w4 = pack_lane<BF16>([&](int e) { return kn(ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3), dk); });
-    reinterpret_cast<uint4*>(kqb + (Gm::KTA + tile) * kTileBytes)[ln] = w4;
+    const int dt = tile / KSC, ks = tile % KSC;
+    const int dk = 16 * dt + (ln & 15), g = ln >> 4;
+    float kv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kv[e] = kn(ks * SK + (e >> 2) * 16 + 4 * g + (e & 3), dk);
+    kt[tile * 64 + ln] = pack(kv);
+    for (int hi = 0; hi < G; ++hi) {
+      const float* dk_h = dkf + hi * kC;
+      float dv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dv[e] = kv[e] * dk_h[ks * SK + (e >> 2) * 16 + 4 * g + (e & 3)];
+      reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::KDA + tile) * kTileBytes)[ln] = pack(dv);
+    }
   }
   __syncthreads();
 
-  // ---- A = K K^T and B = Q K^T (lower 16x16 tiles incl. the diagonal) ----
-  for (int task = wave; task < 20; task += kChunkThreads / 64) {
-    const int which = task / 10;  // 0: K K^T, 1: Q K^T
-    int t = task % 10, ti = 0;
-    while (t > ti) { t -= ti + 1; ++ti; }
-    const int tj = t;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF16) {
-      // K K^T (which feeds the inverse) sums hi*hi + hi*lo + lo*hi for about
-      // fp32 accuracy; Q K^T (stored as bf16) takes one product.  A packed
-      // K tile is also the B operand of K^T (same lanes, same k order).
-      const uint4* khi = pk;
-      const uint4* klo = pk + 4 * KSD * 64;
-      const uint4* qq = pk + 2 * 4 * KSD * 64;
+  // ---- K K^T (lower 16x16 tiles) into LDS; K Q^T read as packed P tiles of
+  // every v-head (workspace) ----
+  {
+    constexpr int NPT = TriTiles<BF16>::count();
+    const uint4* kh_t = pk;
+    const uint4* kl_t = pk + 4 * KSD * 64;
+    const uint4* q_t = pk + Sm::PK_Q * 4 * KSD * 64;
+    for (int task = wave; task < 10 + NPT; task += kChunkWaves) {
+      if (task < 10) {
+        int t = task, ti = 0;
+        while (t > ti) { t -= ti + 1; ++ti; }
+        const int tj = t;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, khi[(tj * KSD + ks) * 64 + lane]);
-        if (which == 0) {
-          const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, khi[(ti * KSD + ks) * 64 + lane]);
-          const bf16x8_t al = __builtin_bit_cast(bf16x8_t, klo[(ti * KSD + ks) * 64 + lane]);
-          const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, klo[(tj * KSD + ks) * 64 + lane]);
-          acc = mfma32(ah, bh, acc);
-          acc = mfma32(ah, bl, acc);
-          acc = mfma32(al, bh, acc);
+        for (int ks = 0; ks < KSD; ++ks) {
+          const uint4 ah = kh_t[(ti * KSD + ks) * 64 + lane];
+          const Bop bh = __builtin_bit_cast(Bop, kh_t[(tj * KSD + ks) * 64 + lane]);
+          acc = Ch::step(ah, bh, acc);
+          if constexpr (BF16) {
+            // K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about fp32 accuracy
+            acc = Ch::step(ah, __builtin_bit_cast(Bop, kl_t[(tj * KSD + ks) * 64 + lane]), acc);
+            acc = Ch::step(kl_t[(ti * KSD + ks) * 64 + lane], bh, acc);
+          }
+        }
+        const int g = lane >> 4, j = 16 * tj + (lane & 15);
+        if (G <= NH) {
+          // one inverse group: L_rj = beta_r e^{G_r - G_j} (k_r . k_j), r > j, of every
+          // v-head straight from the accumulator; the mirrored block above the
+          // diagonal is zero
+          for (int hi = 0; hi < G; ++hi) {
+            const float* gc = gcum + hi * kC;
+            const float gj = gc[j];
+            float* Lh = Lt + hi * kC * kLd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * ti + 4 * g + i;
+              Lh[r * kLd + j] = j < r ? bet[hi * kC + r] * __expf(gc[r] - gj) * acc[i] : 0.f;
+              if (ti != tj) Lh[(16 * tj + 4 * g + i) * kLd + 16 * ti + (lane & 15)] = 0.f;
+            }
+          }
         } else {
-          acc = mfma32(__builtin_bit_cast(bf16x8_t, qq[(ti * KSD + ks) * 64 + lane]), bh, acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Am[(ti * 16 + g * 4 + i) * kLd + j] = acc[i];
+        }
+      } else {
+        int ti, ks;
+        TriTiles<BF16>::at(task - 10, ti, ks);
+        // (K Q^T)[j][r] with j = 16 tj + 4g + i, r = 16 ti + (lane & 15): the
+        // accumulator of tile (tj, ti) is packed P tile (ti, ks) element (tj%TPS)*4 + i
+        f32x4_t acc[TPS];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+          const int tj = TPS * ks + u;
+          acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (tj <= ti) {
+#pragma unroll
+            for (int kd = 0; kd < KSD; ++kd)
+              acc[u] = Ch::step(kh_t[(tj * KSD + kd) * 64 + lane],
+                                __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]), acc[u]);
+          }
+        }
+        const int r = 16 * ti + (lane & 15), g = lane >> 4;
+        for (int hi = 0; hi < G; ++hi) {
+          const float* gc = gcum + hi * kC;
+          const float gr = gc[r];
+          float pv[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+            pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
+          }
+          reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes)[lane] = pack(pv);
         }
       }
-    } else {
-      const int ra = ti * 16 + (lane & 15), rb = tj * 16 + (lane & 15), kk = lane >> 4;
-      for (int k0 = 0; k0 < D; k0 += 4) {
-        const float av = which == 0 ? kn(ra, k0 + kk) : qn(ra, k0 + kk);
-        acc = mfma4(av, kn(rb, k0 + kk), acc);
-      }
     }
-    float* out = which == 0 ? Am : Bm;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[(ti * 16 + (lane >> 4) * 4 + i) * kLd + tj * 16 + (lane & 15)] = acc[i];
   }
   __syncthreads();
 
-  // ---- per v-head: L (LDS), P and T (packed, workspace) ----
-  for (int hg0 = 0; hg0 < G; hg0 += 4) {
-    const int nh = min(4, G - hg0);
-    for (int e = tid; e < nh * kC * kC; e += kChunkThreads) {
-      const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
-      const float* gc = gcum + (hg0 + i) * kC;
-      Lt[i * kC * kLd + r * kLd + j] = j < r ? bet[(hg0 + i) * kC + r] * __expf(gc[r] - gc[j]) * Am[r * kLd + j] : 0.f;
+  // ---- per group of NH v-heads: L, T = (I + L)^{-1}, then -W and U' ----
+  for (int hg0 = 0; hg0 < G; hg0 += NH) {
+    const int nh = min(NH, G - hg0);
+    if (G > NH) {  // several groups: L of this group from K K^T in LDS
+      for (int e = tid; e < nh * kC * kC; e += kChunkThreads) {
+        const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
+        const float* gc = gcum + (hg0 + i) * kC;
+        Lt[i * kC * kLd + r * kLd + j] = j < r ? bet[(hg0 + i) * kC + r] * __expf(gc[r] - gc[j]) * Am[r * kLd + j] : 0.f;
+      }
+      __syncthreads();
     }
-    for (int u = tid; u < nh * 4 * KSC * 64; u += kChunkThreads) {
-      const int i = u / (4 * KSC * 64), tile = (u >> 6) % (4 * KSC), ln = u & 63;
-      const int mt = tile / KSC, ks = tile % KSC;
-      const int r = 16 * mt + (ln & 15), g = ln >> 4;
-      const float* gc = gcum + (hg0 + i) * kC;
-      const uint4 w4 = pack_lane<BF16>([&](int e) {
-        const int j = ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3);
-        return j <= r ? __expf(gc[r] - gc[j]) * Bm[r * kLd + j] : 0.f;
-      });
-      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::PA + tile) * kTileBytes)[ln] = w4;
-    }
-    __syncthreads();
     if (wave < nh) invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
     __syncthreads();
-    for (int u = tid; u < nh * 4 * KSC * 64; u += kChunkThreads) {
-      const int i = u / (4 * KSC * 64), tile = (u >> 6) % (4 * KSC), ln = u & 63;
+    // T diag(beta e^G) (for W) and T diag(beta) (for U') as A tiles; the
+    // identically zero tiles above the diagonal are never read
+    for (int u = tid; u < nh * 2 * 4 * KSC * 64; u += kChunkThreads) {
+      const int tile = (u >> 6) % (4 * KSC), which = (u >> 6) / (4 * KSC) % 2, i = (u >> 6) / (8 * KSC);
+      const int ln = u & 63;
       const int mt = tile / KSC, ks = tile % KSC;
+      if (ks * SK > 16 * mt + 15) continue;
       const int r = 16 * mt + (ln & 15), g = ln >> 4;
-      const float* Ti = Lt + i * kC * kLd;
-      const uint4 w4 = pack_lane<BF16>([&](int e) { return Ti[r * kLd + ks * P::SK + (e >> 2) * 16 + 4 * g + (e & 3)]; });
-      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::TA + tile) * kTileBytes)[ln] = w4;
+      const float* Ti = Lt + i * kC * kLd + r * kLd;
+      const float* sc = (which == 0 ? bge : bet) + (hg0 + i) * kC;
+      float tv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        tv[e] = Ti[j] * sc[j];
+      }
+      tt[((i * 2 + which) * 4 * KSC + tile) * 64 + ln] = pack(tv);
     }
     __syncthreads();
+    // U' = T diag(beta) V: task (head, dvt) makes the 4 token tiles of 16
+    // columns.  The V tiles come from the workspace (L2), so every wave
+    // issues the loads of all its U' tasks first and runs its -W tasks
+    // (operands in LDS) while they are in flight.
+    constexpr int MAXV = (NH * NT + kChunkWaves - 1) / kChunkWaves;
+    const int nv = nh * NT;
+    Bop vop[MAXV][KSC];
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int t = min(wave + k * kChunkWaves, nv - 1);  // a clamped duplicate is loaded, never used
+      const int i = t / NT, dvt = t % NT;
+      const E* vb = reinterpret_cast<const E*>(headb(kh * G + hg0 + i) + Gm::VB_OFF) + dvt * 4 * 256 + lane * 4;
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        if constexpr (BF16) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vb + (2 * ks) * 256);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vb + (2 * ks + 1) * 256);
+          vop[k][ks] = __builtin_bit_cast(Bop, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          vop[k][ks] = __builtin_bit_cast(Bop, *reinterpret_cast<const uint4*>(vb + ks * 256));
+        }
+      }
+    }
+    // -W = -(T diag(beta e^G)) K: W^T = K^T (T diag(beta e^G))^T, tile (dt, mt)
+    // accumulators read as packed A tile (mt, ksd) of W (rows token, k = d)
+    const int nw = nh * 4 * KSD;
+    for (int task = wave; task < nw; task += kChunkWaves) {
+      const int i = task / (4 * KSD), mt = (task / KSD) % 4, ksd = task % KSD;
+      const int kmax = (16 * mt + 15) / SK;
+      const uint4* tw = tt + (i * 2 + 0) * 4 * KSC * 64;
+      f32x4_t acc[TPS];
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const int dt = TPS * ksd + u;
+        acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (dt < NT) {
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks <= kmax)
+              acc[u] = Ch::step(kt[(dt * KSC + ks) * 64 + lane],
+                                __builtin_bit_cast(Bop, tw[(mt * KSC + ks) * 64 + lane]), acc[u]);
+        }
+      }
+      float wv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) wv[e] = -acc[e >> 2][e & 3];
+      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::WA + mt * KSD + ksd) * kTileBytes)[lane] = pack(wv);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int t = wave + k * kChunkWaves;
+      if (t < nv) {
+        const int i = t / NT, dvt = t % NT;
+        const uint4* tb = tt + (i * 2 + 1) * 4 * KSC * 64;
+        E* vw = reinterpret_cast<E*>(headb(kh * G + hg0 + i) + Gm::VW_OFF) + dvt * 4 * 256 + lane * 4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks * SK <= 16 * mt + 15) acc = Ch::step(tb[(mt * KSC + ks) * 64 + lane], vop[k][ks], acc);
+          if constexpr (BF16) {
+            uint2 pkd;
+            pkd.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
+            pkd.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[3])) << 16);
+            *reinterpret_cast<uint2*>(vw + mt * 256) = pkd;
+          } else {
+            *reinterpret_cast<float4*>(vw + mt * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // Lt and the T tiles are reused by the next group
   }
 }
 
 // ---------------------------------------------------------------------------
 // chain: sequential chunk loop, one wave per 16 rows of d_v
 // ---------------------------------------------------------------------------
+constexpr int kLoaders = 2;  // loader waves per chain workgroup
+
 template <int D, bool BF16, int CW>
 struct ChainSmem {
   using Gm = Geo<D, BF16>;
-  static constexpr size_t KQ = Gm::KQ_BYTES;
-  static constexpr size_t TP = 8 * Gm::KSC * kTileBytes;
-  static constexpr size_t VC = CW * 4 * Pk<BF16>::VC_BYTES;
+  static constexpr size_t KQ = Gm::KQ_BYTES;                       // Q tiles of the k-head
+  static constexpr size_t HT = Gm::HT_TILES * kTileBytes;          // -W, K^T decayed, P of the v-head
+  static constexpr size_t VW = CW * 4 * Pk<BF16>::VC_BYTES;        // U' tiles of this workgroup's rows
   static constexpr size_t GATES = Gm::GATE_BYTES;
-  static constexpr size_t BUF = KQ + TP + VC + GATES;
-  static constexpr int UNITS = static_cast<int>(BUF / 16);           // 16-byte units per buffer
-  static constexpr int NBUF = 2 * BUF <= 150 * 1024 ? 2 : 1;
-  static constexpr size_t BYTES = NBUF * BUF;
+  static constexpr size_t BYTES = KQ + HT + VW + GATES;
+  // the loader waves copy whole rounds of kLoaders x 64 x 16 bytes
+  static constexpr size_t ROUND = kLoaders * 64 * 16;
+  static constexpr size_t BUF = (BYTES + ROUND - 1) / ROUND * ROUND;
+  static_assert(2 * BUF <= 150 * 1024, "two chunk buffers must fit in LDS");
 };
 
+// Workgroup -> (sequence, v-head, block of CW x 16 rows of d_v).  Workgroups
+// are dispatched to the 8 XCDs round robin by linear id; the logical index
+// q = (s * Hv + h) * Z + z is spread so that consecutive q (the workgroups of
+// one k-head, which read the same Q tiles, and of one v-head, which read the
+// same W, K^T and P tiles) share an XCD and its L2.
+__device__ __forceinline__ int chain_logical_index(int L, int nwg) {
+  return (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
+}
+
+// Chain workgroup: CW compute waves (wave w holds rows 16 (z CW + w) ..) and
+// kLoaders loader waves.  While the compute waves work on chunk c from one
+// LDS buffer, the loaders copy chunk c+1 (the Q tiles of the k-head, the -W /
+// K^T / P tiles of the v-head, this workgroup's U' tiles and the gate factors)
+// into the other; one workgroup barrier per chunk swaps the buffers.  The
+// waves of a workgroup sit on different SIMDs, so the copies cost the
+// compute waves no issue slots.
 template <int D, bool BF16, int CW>
-__global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, PrefillLayout Lay) {
+__global__ __launch_bounds__((CW + kLoaders) * 64, 1) void chain_kernel(PrefillArgs A, PrefillLayout Lay) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ChainSmem<D, BF16, CW>;
   using Ch = Chain<BF16>;
   using E = typename P::E;
   using Bop = typename Ch::Bop;
-  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT;
-  constexpr int TPS = P::SK / 16;                 // accumulator tiles per packed super-step
-  constexpr int U_KQ = static_cast<int>(Sm::KQ / 16);
-  constexpr int U_TP = U_KQ + static_cast<int>(Sm::TP / 16);
-  constexpr int U_VC = U_TP + static_cast<int>(Sm::VC / 16);
+  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT, TPS = Gm::TPS, Z = NT / CW;
   __shared__ __attribute__((aligned(1024))) char lds0[Sm::BUF];
-  __shared__ __attribute__((aligned(1024))) char lds1[Sm::NBUF == 2 ? Sm::BUF : 16];
+  __shared__ __attribute__((aligned(1024))) char lds1[Sm::BUF];
 
-  const int s = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int dvt = blockIdx.z * CW + wave;        // this wave's 16 rows of d_v
+  const int q = chain_logical_index(blockIdx.x, gridDim.x);
+  const int zb = q % Z, h = (q / Z) % A.Hv, s = q / (Z * A.Hv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int dvt = zb * CW + wave;                // a compute wave's 16 rows of d_v
   const int32_t* se = ws_ptr<int32_t>(A.workspace, Lay.seq_tab) + 8 * s;
   if (!(se[SQ_FLAGS] & SQF_VALID)) return;
   const bool init = (se[SQ_FLAGS] & SQF_INIT) != 0;
@@ -698,13 +902,79 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
   const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, kh = h / G;
   const int g = lane >> 4, col = lane & 15;
-
-  // ---- S^T slice in accumulators: tile i holds S^T[16i + 4g + e][16 dvt + col] ----
+  // This launch covers the sequence's chunks in [c0, c1) of the chunk table;
+  // the state carries over between launches through the slot (fp32, exact).
+  // A sequence without chunks belongs to the launch that starts at chunk 0.
+  const int c0 = max(first, A.seg_lo), c1 = min(first + nc, A.seg_hi);
+  if (nc == 0 ? A.seg_lo != 0 : c0 >= c1) return;
+  const bool seq_first = nc == 0 || c0 == first;     // the sequence starts in this launch
+  const bool seq_last = nc == 0 || c1 == first + nc;  // ... and ends in it
+  const bool state_in = seq_first ? init : true;
+  const int cr0 = c0 - first, ncl = c1 - c0;          // first chunk (within the sequence) and count
   float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
+
+  // ---- loader waves ----
+  if (wave >= CW) {
+    const int lw = wave - CW;
+    const char* wsb = static_cast<const char*>(A.workspace);
+    // 1 KB blocks [Q | -W, K^T, P | U' | gates]; loader lw copies blocks
+    // kLoaders j + lw.  Every segment starts at a multiple of kLoaders blocks,
+    // so the segment of round j is known at compile time.
+    constexpr int NKQ = static_cast<int>(Sm::KQ / 1024), NHT = static_cast<int>(Sm::HT / 1024);
+    constexpr int NVW = static_cast<int>(Sm::VW / 1024), NBLK = NKQ + NHT + NVW + 1;
+    constexpr int NJ = (NBLK + kLoaders - 1) / kLoaders;
+    static_assert(NKQ % kLoaders == 0 && NHT % kLoaders == 0 && NVW % kLoaders == 0 && Sm::VW % 1024 == 0,
+                  "segment alignment");
+    static_assert(Sm::GATES <= 1024, "gates fit one block");
+    auto load_chunk = [&](int chunk, char* base) {
+      const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
+      const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
+      const char* vwb = hb + Gm::VW_OFF + static_cast<size_t>(zb) * CW * 4 * P::VC_BYTES;
+      // an opaque copy of this lane's offset: keeps the compiler from hoisting
+      // one address register per block out of the chunk loop, which would leave
+      // no registers for loads in flight
+      int lo = lw * 1024 + lane * 16;
+      asm volatile("" : "+v"(lo));
+      constexpr int NB = (NJ + 31) / 32, KB = (NJ + NB - 1) / NB;  // at most 32 loads in flight
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        uint4 r[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const int j = bt * KB + k;
+          if (j >= NJ) break;
+          const int b0 = j * kLoaders;               // first block of this round
+          const char* src;
+          if (b0 < NKQ) src = kq + b0 * 1024;
+          else if (b0 < NKQ + NHT) src = hb + (b0 - NKQ) * 1024;
+          else if (b0 < NKQ + NHT + NVW) src = vwb + (b0 - NKQ - NHT) * 1024;
+          else src = hb + Gm::GATE_OFF - lw * 1024;  // gates: loader 0, lanes < GATES / 16
+          r[k] = (b0 + kLoaders <= NKQ + NHT + NVW || (lw == 0 && lane * 16 < static_cast<int>(Sm::GATES)))
+                     ? *reinterpret_cast<const uint4*>(src + lo)
+                     : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const int j = bt * KB + k;
+          if (j >= NJ) break;
+          *reinterpret_cast<uint4*>(base + j * kLoaders * 1024 + lo) = r[k];
+        }
+      }
+    };
+    if (ncl > 0) load_chunk(c0, lds0);
+    lds_barrier();
+#pragma clang loop unroll(disable)
+    for (int ci = 0; ci < ncl; ++ci) {
+      if (ci + 1 < ncl) load_chunk(c0 + ci + 1, (ci & 1) ? lds0 : lds1);
+      lds_barrier();
+    }
+  } else {
+
+  // ---- compute waves: S^T slice in accumulators, tile i holds S^T[16i + 4g + e][16 dvt + col] ----
   f32x4_t st[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    if (init) {
+    if (state_in) {
       const float4 v = *reinterpret_cast<const float4*>(Sglob + 16 * i + 4 * g);
       st[i] = f32x4_t{v.x, v.y, v.z, v.w};
     } else {
@@ -712,45 +982,42 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
     }
   }
 
-  // Staging of one chunk into one LDS buffer with direct global->LDS loads:
-  // the packed K/Q/K^T block of the k-head, the T/P tiles, this workgroup's V
-  // tiles and the gate factors of the head.  The two buffers are distinct LDS
-  // arrays, so loads landing in one never make the compiler wait before
-  // reading the other.
-  const char* wsb = static_cast<const char*>(A.workspace);
-  // Every 1 KB block of the buffer lies in one segment (the segment sizes are
-  // multiples of 1 KB), so the source base is wave-uniform and each lane adds
-  // its 16-byte offset.
-  static_assert(Sm::KQ % 1024 == 0 && Sm::TP % 1024 == 0 && Sm::VC % 512 == 0, "segment alignment");
-  auto stage = [&](int chunk, char* base) {
-    const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
-    const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
-    const char* vcb = hb + Gm::VC_OFF + static_cast<size_t>(blockIdx.z) * CW * 4 * P::VC_BYTES;
-    constexpr int NKQ = static_cast<int>(Sm::KQ / 1024), NTP = static_cast<int>(Sm::TP / 1024);
-    auto dma = [&](const char* src, char* dst, int lim) {
-      if (lane * 16 < lim)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src) + lane,
-                                         (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
-    };
-    for (int b = wave; b < NKQ; b += CW) dma(kq + b * 1024, base + b * 1024, 1024);
-    for (int b = wave; b < NTP; b += CW) dma(hb + b * 1024, base + Sm::KQ + b * 1024, 1024);
-    for (int b = wave; b * 1024 < static_cast<int>(Sm::VC); b += CW)
-      dma(vcb + b * 1024, base + Sm::KQ + Sm::TP + b * 1024, static_cast<int>(Sm::VC) - b * 1024);
-    if (wave == CW - 1) dma(hb + Gm::GATE_OFF, base + Sm::KQ + Sm::TP + Sm::VC, static_cast<int>(Sm::GATES));
-  };
-  auto wait_stage = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
-    lds_barrier();                  // ... and everyone else's
-  };
-
-  // One chunk step from LDS buffer buf; O returned in registers.
+  // One chunk step from an LDS buffer; O returned in registers.  The body
+  // runs in stages separated by scheduling barriers: every stage issues the
+  // LDS reads of the operand tiles the NEXT stage multiplies, so those reads
+  // are in flight while this stage's MFMAs run (a wave has no other wave on
+  // its SIMD to hide LDS latency behind).
   auto compute = [&](const char* base, f32x4_t (&O)[4]) {
-    const uint4* kq = reinterpret_cast<const uint4*>(base);
-    const uint4* tp = reinterpret_cast<const uint4*>(base + Sm::KQ);
-    const E* vc = reinterpret_cast<const E*>(base + Sm::KQ + Sm::TP) + wave * 4 * 256;
-    const float* gt = reinterpret_cast<const float*>(base + Sm::KQ + Sm::TP + Sm::VC);
-    auto tileA = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
+    const uint4* qa = reinterpret_cast<const uint4*>(base);
+    const uint4* ht = reinterpret_cast<const uint4*>(base + Sm::KQ);
+    const E* vw = reinterpret_cast<const E*>(base + Sm::KQ + Sm::HT) + wave * 4 * 256;
+    const float* gt = reinterpret_cast<const float*>(base + Sm::KQ + Sm::HT + Sm::VW);
+    auto tile = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
+    auto fence = [] {
+#if GDN_CHAIN_SCHED
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+    };
 
+    // stage 0: -W tiles, U', e^{G_last}
+    uint4 wa[4][KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) wa[mt][ks] = tile(ht + Gm::WA * 64, mt * KSD + ks);
+    f32x4_t U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if constexpr (BF16) {
+        const uint2 r2 = *reinterpret_cast<const uint2*>(vw + mt * 256 + lane * 4);
+        U[mt] = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                        __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
+      } else {
+        const float4 r4 = *reinterpret_cast<const float4*>(vw + mt * 256 + lane * 4);
+        U[mt] = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+      }
+    }
+    const float eGl = gt[kC];
     // B operands of S^T (d_k in packed order)
     Bop bS[KSD];
 #pragma unroll
@@ -758,79 +1025,62 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
       const int i0 = ks * TPS;
       bS[ks] = Ch::bop(st[i0], (TPS == 2 && i0 + 1 < NT) ? st[(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
     }
-    // X = K S^T and Y = Q S^T for the 4 token tiles
-    f32x4_t X[4], Y[4];
+    fence();
+    // stage 1: U = U' - W S^T; read the Q tiles
+    uint4 qt[4][KSD];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      X[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        X[mt] = Ch::step(tileA(kq + Gm::KA * 64, mt * KSD + ks), bS[ks], X[mt]);
-        Y[mt] = Ch::step(tileA(kq + Gm::QA * 64, mt * KSD + ks), bS[ks], Y[mt]);
-      }
-    }
-    // R = beta V - (beta e^G) X for this lane's tokens 16 mt + 4 g + i
-    f32x4_t Rt[4];
+      for (int mt = 0; mt < 4; ++mt) qt[mt][ks] = tile(qa, mt * KSD + ks);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 c1 = *reinterpret_cast<const float4*>(gt + kC + 16 * mt + 4 * g);
-      float vv[4];
-      if constexpr (BF16) {
-        const uint2 r2 = *reinterpret_cast<const uint2*>(vc + mt * 256 + lane * 4);
-        vv[0] = __uint_as_float(r2.x << 16); vv[1] = __uint_as_float(r2.x & 0xffff0000u);
-        vv[2] = __uint_as_float(r2.y << 16); vv[3] = __uint_as_float(r2.y & 0xffff0000u);
-      } else {
-        const float4 r4 = *reinterpret_cast<const float4*>(vc + mt * 256 + lane * 4);
-        vv[0] = r4.x; vv[1] = r4.y; vv[2] = r4.z; vv[3] = r4.w;
-      }
-      Rt[mt][0] = fmaf(-c1.x, X[mt][0], vv[0]);
-      Rt[mt][1] = fmaf(-c1.y, X[mt][1], vv[1]);
-      Rt[mt][2] = fmaf(-c1.z, X[mt][2], vv[2]);
-      Rt[mt][3] = fmaf(-c1.w, X[mt][3], vv[3]);
-    }
-    // U = T R (T lower triangular: token tile mt needs j < 16 (mt + 1))
-    Bop bR[KSC];
+    for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) bR[ks] = Ch::bop(Rt[ks * TPS], Rt[(ks * TPS + 1) % 4]);
-    f32x4_t U[4];
+      for (int mt = 0; mt < 4; ++mt) U[mt] = Ch::step(wa[mt][ks], bS[ks], U[mt]);
+    fence();
+    // stage 2: Y = Q S^T, S^T scaled by e^{G_last}; read the decayed K^T tiles
+    uint4 kd[NT][KSC];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      U[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) kd[i][ks] = tile(ht + Gm::KDA * 64, i * KSC + ks);
+    f32x4_t Y[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Y[mt] = Ch::step(qt[mt][ks], bS[ks], Y[mt]);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) st[i] = st[i] * eGl;
+    Bop bU[KSC];
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) bU[ks] = Ch::bop(U[ks * TPS], U[(ks * TPS + 1) % 4]);
+    fence();
+    // stage 3: S^T <- e^{G_last} S^T + (diag(e^{G_last - G}) K)^T U; read the P tiles and e^G
+    uint4 pt[4][KSC];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks)
-        if (ks * P::SK < 16 * (mt + 1)) U[mt] = Ch::step(tileA(tp + Gm::TA * 64, mt * KSC + ks), bR[ks], U[mt]);
-    }
-    // O = diag(e^G) Y + P U;  Ut = diag(e^{G_last - G}) U
-    f32x4_t Ut[4];
+        if (ks * P::SK < 16 * (mt + 1)) pt[mt][ks] = tile(ht + Gm::PA * 64, mt * KSC + ks);
+    float4 eg[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 dc = *reinterpret_cast<const float4*>(gt + 2 * kC + 16 * mt + 4 * g);
-      Ut[mt] = U[mt] * f32x4_t{dc.x, dc.y, dc.z, dc.w};
-    }
-    Bop bU[KSC], bUt[KSC];
+    for (int mt = 0; mt < 4; ++mt) eg[mt] = *reinterpret_cast<const float4*>(gt + 16 * mt + 4 * g);
 #pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) {
-      bU[ks] = Ch::bop(U[ks * TPS], U[(ks * TPS + 1) % 4]);
-      bUt[ks] = Ch::bop(Ut[ks * TPS], Ut[(ks * TPS + 1) % 4]);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 eg = *reinterpret_cast<const float4*>(gt + 16 * mt + 4 * g);
-      f32x4_t o = Y[mt] * f32x4_t{eg.x, eg.y, eg.z, eg.w};
+    for (int ip = 0; ip < NT; ip += 2)
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks)
-        if (ks * P::SK < 16 * (mt + 1)) o = Ch::step(tileA(tp + Gm::PA * 64, mt * KSC + ks), bU[ks], o);
+#pragma unroll
+        for (int i = ip; i < ip + 2 && i < NT; ++i) st[i] = Ch::step(kd[i][ks], bU[ks], st[i]);
+    fence();
+    // stage 4: O = diag(e^G) Y + P U
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4_t o = Y[mt] * f32x4_t{eg[mt].x, eg[mt].y, eg[mt].z, eg[mt].w};
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks)
+        if (ks * P::SK < 16 * (mt + 1)) o = Ch::step(pt[mt][ks], bU[ks], o);
       O[mt] = o;
-    }
-    // S^T <- e^{G_last} S^T + K^T Ut
-    const float eGl = gt[3 * kC];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      f32x4_t acc = st[i] * eGl;
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) acc = Ch::step(tileA(kq + Gm::KTA * 64, i * KSC + ks), bUt[ks], acc);
-      st[i] = acc;
     }
   };
 
@@ -853,49 +1103,30 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
     }
   };
 
-  if (nc > 0) {
+  {
     f32x4_t O[4];
-    stage(first, lds0);
-    wait_stage();
-    for (int ci = 0; ci < nc; ci += 2) {
-      if (Sm::NBUF == 2) {
-        if (ci + 1 < nc) stage(first + ci + 1, lds1);
-        if (ci > 0) store_o(ci - 1, O);
-        compute(lds0, O);
-        wait_stage();
-        if (ci + 1 < nc) {
-          if (ci + 2 < nc) stage(first + ci + 2, lds0);
-          store_o(ci, O);
-          compute(lds1, O);
-          wait_stage();
-        }
-      } else {
-        if (ci > 0) store_o(ci - 1, O);
-        compute(lds0, O);
-        if (ci + 1 < nc) {
-          lds_barrier();
-          stage(first + ci + 1, lds0);
-          wait_stage();
-          store_o(ci, O);
-          compute(lds0, O);
-          if (ci + 2 < nc) {
-            lds_barrier();
-            stage(first + ci + 2, lds0);
-            wait_stage();
-          }
-        }
+    lds_barrier();  // the first chunk staged
+    for (int ci = 0; ci < ncl; ci += 2) {
+      if (ci > 0) store_o(cr0 + ci - 1, O);
+      compute(lds0, O);
+      lds_barrier();
+      if (ci + 1 < ncl) {
+        store_o(cr0 + ci, O);
+        compute(lds1, O);
+        lds_barrier();
       }
     }
-    store_o(nc - 1, O);
+    if (ncl > 0) store_o(cr0 + ncl - 1, O);
   }
 
   // ---- final state back to the slot ----
 #pragma unroll
   for (int i = 0; i < NT; ++i)
     *reinterpret_cast<float4*>(Sglob + 16 * i + 4 * g) = make_float4(st[i][0], st[i][1], st[i][2], st[i][3]);
+  }  // compute waves
 
   // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
-  if (A.W > 0) {
+  if (A.W > 0 && seq_last) {
     const int W = A.W, C = A.C, R = A.R;
     const uint32_t pos_end = (init ? pos0 : 0u) + static_cast<uint32_t>(len);
     float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
@@ -907,35 +1138,61 @@ __global__ __launch_bounds__(CW * 64, 1) void chain_kernel(PrefillArgs A, Prefil
         else if (!init) *dst = 0.f;
       }
     };
-    if (h % G == 0 && blockIdx.z == 0)
-      for (int cc = tid; cc < 2 * D; cc += CW * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
-    if (lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
-    if (h == 0 && blockIdx.z == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
+    if (h % G == 0 && zb == 0)
+      for (int cc = tid; cc < 2 * D; cc += (CW + kLoaders) * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
+    if (wave < CW && lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
+    if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Launcher
 // ---------------------------------------------------------------------------
+// Chunks per launch segment: the workspace of one segment (about 4.4 MB per
+// chunk at 16 k-heads / 48 v-heads / d = 128) stays resident in the 256 MB
+// last-level cache between the chunk kernel that writes it and the chain
+// kernel that reads it.
+constexpr int kSegChunks = 16;
+
 template <int D, bool BF16>
-static int launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  constexpr int CW = Geo<D, BF16>::NT < 2 ? Geo<D, BF16>::NT : 2;
-  const PrefillLayout L = layout_t<D, BF16>(a.Hk, a.Hv, a.max_chunks, a.n_seqs);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a, L);
+static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
+  constexpr int CWMAX = BF16 ? 4 : 2;
+  constexpr int CW = Geo<D, BF16>::NT < CWMAX ? Geo<D, BF16>::NT : CWMAX;
+  const PrefillLayout L = layout_t<D, BF16>(a0.Hk, a0.Hv, a0.max_chunks, a0.n_seqs);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L);
   int e = static_cast<int>(hipGetLastError());
   if (e) return e;
   const size_t smem = ChunkSmem<D, BF16>::BYTES;
-  e = static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<D, BF16>),
+  auto chunk_fn = a0.W == 4 ? &chunk_kernel<D, BF16, 4> : &chunk_kernel<D, BF16, 0>;
+  e = static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
   if (e) return e;
-  if (a.max_chunks > 0) {
-    hipLaunchKernelGGL((chunk_kernel<D, BF16>), dim3(a.max_chunks, a.Hk), dim3(kChunkThreads), smem, st, a, L);
+  // at least one segment, so that sequences without tokens still get their slot written
+  for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks) {
+    PrefillArgs a = a0;
+    a.seg_lo = lo;
+    a.seg_hi = lo + kSegChunks;
+    const int n = a0.max_chunks - lo < kSegChunks ? a0.max_chunks - lo : kSegChunks;
+    if (n > 0) {
+      hipLaunchKernelGGL(chunk_fn, dim3(n, a.Hk), dim3(kChunkThreads), smem, st, a, L);
+      e = static_cast<int>(hipGetLastError());
+      if (e) return e;
+    }
+    hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(a.n_seqs * a.Hv * (Geo<D, BF16>::NT / CW)),
+                       dim3((CW + kLoaders) * 64), 0, st, a, L);
     e = static_cast<int>(hipGetLastError());
     if (e) return e;
   }
-  hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(a.n_seqs, a.Hv, Geo<D, BF16>::NT / CW), dim3(CW * 64), 0,
-                     st, a, L);
-  return static_cast<int>(hipGetLastError());
+  return 0;
+}
+
+template <int D, bool BF16>
+static int launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  if constexpr (ChunkSmem<D, BF16>::BYTES > 160 * 1024) {
+    return static_cast<int>(hipErrorInvalidValue);  // refused by the API before any launch
+  } else {
+    return launch_prefill_fit<D, BF16>(a, st);
+  }
 }
 
 int launch_prefill(const PrefillArgs& a, bool bf16, void* stream) {

@@ -93,8 +93,9 @@ def test_workspace_size(gdn):
     n1 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 8192, 1)
     n2 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 16384, 1)
     assert n1 > 0 and n2 > n1
-    # per 64-token chunk: q, k, k^T (16 heads) + v, T, P (48 heads) in bf16 + fp32 gates
-    per_chunk = 3 * 16 * 64 * 128 * 2 + 48 * 64 * 128 * 2 + 2 * 48 * 64 * 64 * 2 + 2 * 48 * 64 * 4
+    # per 64-token chunk: q tiles (16 k-heads); per v-head (48): -W, decayed K^T,
+    # U' and V (64 x 128 bf16 each), P (64 x 64 bf16) and two fp32 gate rows
+    per_chunk = 16 * 64 * 128 * 2 + 48 * (4 * 64 * 128 * 2 + 64 * 64 * 2 + 2 * 64 * 4)
     assert abs(n1 - 129 * per_chunk) < 64 * 1024
     bad = _geom(gdn, n_v_heads=47)
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(bad), 8192, 1) == 0
@@ -152,6 +153,9 @@ def test_prefill_refusals(gdn):
     assert call(n_seqs=9) == 5
     assert call(n_tokens=-1) == 5
     assert call(cu=None) == 1
+    g.dtype_in = g.dtype_out = gdn.GDN_F32
+    assert call() == 4
+    assert "d_k: 128 with dtype_in GDN_F32" in L.gdn_last_error().decode()
 
 
 def test_conv_step_refusals(gdn):
