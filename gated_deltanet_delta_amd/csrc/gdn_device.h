@@ -69,11 +69,42 @@ __device__ __forceinline__ float silu_f(float y) { return y * sigmoid_f(y); }
 // Reductions inside groups of N consecutive lanes (N a power of two <= 64),
 // always in the same butterfly order, so results are reproducible.
 // ---------------------------------------------------------------------------
+// Sum over aligned groups of N lanes, every lane of a group receiving the
+// total (bitwise the same in every lane: each step adds a lane's value to its
+// partner's, and the partners add the same two numbers).  Lane exchanges up to
+// 16 apart use DPP (quad permutes and row mirrors), 16 and 32 use swizzle /
+// bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = N / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror: partner 7 - i within 8 lanes
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v); // row_mirror: partner 15 - i within 16 lanes
+  if constexpr (N >= 32)                         // swizzle, and mask 31, xor mask 16: partner lane ^ 16
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
+}
+
+// Workgroup barrier that orders LDS traffic only: global loads issued before
+// it stay in flight (a full __syncthreads would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// SiLU and sigmoid with the hardware exp and reciprocal (about 2 ulp).
+__device__ __forceinline__ float sigmoid_fast(float y) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
+__device__ __forceinline__ float silu_fast(float y) {
+  return y * sigmoid_fast(y);
 }
 
 // ---------------------------------------------------------------------------

@@ -127,13 +127,6 @@ __device__ __forceinline__ T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Workgroup barrier that orders LDS traffic only: global loads issued before
-// it stay in flight (a full __syncthreads would wait for them too).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // ---------------------------------------------------------------------------
 // plan: chunk table from cu_seqlens
@@ -241,11 +234,6 @@ struct Chain<false> {
   }
 };
 
-// SiLU with the hardware exp and reciprocal (the front end runs it on every
-// input of every token, so it is kept to five instructions).
-__device__ __forceinline__ float silu_fast(float y) {
-  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
-}
 
 // acc += A (16x16, row-major at a, stride lda) * B (16x16, row-major at b, stride ldb); fp32.
 __device__ __forceinline__ f32x4_t prod16(const float* a, int lda, const float* b, int ldb,

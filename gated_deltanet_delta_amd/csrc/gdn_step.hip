@@ -36,16 +36,8 @@ struct StepShape {
   static constexpr int THREADS = NW * kWave;
 };
 
-// Input of the conv window at relative token `rel` (rel >= 0: draft/current
-// token rel of this batch row; rel < 0: ring row of position pos + rel).
-template <bool BF16>
-__device__ __forceinline__ float4 window_in4(const float* ring, uint32_t pos, int R,
-                                             const void* xb, int C, int rel, int c) {
-  if (rel >= 0) return load_in4<BF16>(xb, static_cast<size_t>(rel) * C + c);
-  return *reinterpret_cast<const float4*>(
-      ring + static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(rel), R)) * C + c);
-}
-
+// Input of the conv window at relative token `rel` (rel >= 0: token rel of
+// this batch row; rel < 0: ring row of position pos + rel).
 template <bool BF16>
 __device__ __forceinline__ float window_in1(const float* ring, uint32_t pos, int R,
                                             const void* xb, int C, int rel, int c) {
@@ -53,41 +45,9 @@ __device__ __forceinline__ float window_in1(const float* ring, uint32_t pos, int
   return ring[static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(rel), R)) * C + c];
 }
 
-// Causal depthwise conv (taps oldest first, tap W-1 on token j) + SiLU for
-// channels c..c+3.  W is a compile-time constant so that every tap's loads are
+// Causal depthwise conv (taps oldest first, tap W-1 on token j) + SiLU of
+// channel c.  W is a compile-time constant so that every tap's loads are
 // issued together; W == 0 passes the input through.
-template <bool BF16, int W>
-__device__ __forceinline__ float4 conv4(const float* ring, uint32_t pos, int R, const void* xb,
-                                        int C, const float* w, int j, int c) {
-  if constexpr (W == 0) {
-    return load_in4<BF16>(xb, static_cast<size_t>(j) * C + c);
-  } else {
-    float4 in[W];
-    float wt[4][W];
-#pragma unroll
-    for (int t = 0; t < W; ++t) in[t] = window_in4<BF16>(ring, pos, R, xb, C, j - (W - 1) + t, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (W == 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(w + (c + i) * 4);
-        wt[i][0] = w4.x; wt[i][1] = w4.y; wt[i][2] = w4.z; wt[i][3] = w4.w;
-      } else {
-#pragma unroll
-        for (int t = 0; t < W; ++t) wt[i][t] = w[(c + i) * W + t];
-      }
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int t = 0; t < W; ++t) {
-      acc.x = fmaf(wt[0][t], in[t].x, acc.x);
-      acc.y = fmaf(wt[1][t], in[t].y, acc.y);
-      acc.z = fmaf(wt[2][t], in[t].z, acc.z);
-      acc.w = fmaf(wt[3][t], in[t].w, acc.w);
-    }
-    return make_float4(silu_f(acc.x), silu_f(acc.y), silu_f(acc.z), silu_f(acc.w));
-  }
-}
-
 template <bool BF16, int W>
 __device__ __forceinline__ float conv1(const float* ring, uint32_t pos, int R, const void* xb,
                                        int C, const float* w, int j, int c) {
@@ -127,124 +87,217 @@ __device__ __forceinline__ float dot4v(f32x4_t a, float4 b) {
 
 // Decode (VERIFY = false: k = 1, state updated in place, position advanced)
 // and verify (VERIFY = true: k drafts, snapshot after each, state untouched).
-template <int D, bool BF16, bool VERIFY, int W>
+//
+// The conv front end is shared by the workgroup: thread t < 2 d_k computes
+// q / k channel t of the k-head, thread t < ROWS_WG the v channel of row t of
+// the workgroup's block, each with its own sliding conv window; results go
+// through a small LDS table (an LDS-only barrier, which leaves the state
+// loads in flight).  Then every lane group updates its state rows as before.
+//
+// Memory order of a call: the slot id and everything that does not depend on
+// it (this token's inputs, conv weights, gates) are requested first; then the
+// ring position; then the state rows (pinned ahead of all arithmetic by a
+// scheduling barrier, so their HBM latency overlaps the rest); then the W-1
+// ring rows of the conv window.
+// RING8: the conv ring has exactly 8 rows, so all of them are read together
+// with the state (no wait on the position before the ring loads) and the
+// window rows are picked in registers.
+template <int D, bool BF16, bool VERIFY, int W, bool RING8>
 __global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A) {
   using Sh = StepShape<D>;
   constexpr int LPR = Sh::LPR;
   constexpr int NP = Sh::NP;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  constexpr int NG = D < kWave ? D : kWave;            // lanes per partial sum of squares
+  static_assert(Sh::THREADS >= 2 * D && Sh::THREADS >= Sh::ROWS_WG, "one channel per thread");
+  __shared__ float fe[2][2 * D + Sh::ROWS_WG];         // q | k | v of a token (two tokens in flight)
+  __shared__ float ssq[2][2 * D / NG];                 // partial sums of squares of q and k
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int hb = blockIdx.x % Sh::WG_PER_HEAD;
   const int h = blockIdx.x / Sh::WG_PER_HEAD;
   const int b = blockIdx.y;
+  const int slot_in = A.slot[b];                       // requested first (scalar load)
   const int G = A.Hv / A.Hk;
   const int kh = h / G;
-  const int c4 = (lane % LPR) * 4;                  // first state column of this lane
-  const int row0 = hb * Sh::ROWS_WG + wave * Sh::ROWS_WAVE + lane / LPR;
+  const int c4 = (lane % LPR) * 4;                     // first state column of this lane
+  const int rloc0 = wave * Sh::ROWS_WAVE + lane / LPR; // this lane's first row within the block
+  const int row0 = hb * Sh::ROWS_WG + rloc0;
+  const int R = A.R, C = A.C;
+  const int kdr = VERIFY ? A.k : 1;
+  const char* xb = static_cast<const char*>(A.x) + static_cast<size_t>(b) * kdr * C * (BF16 ? 2 : 4);
+  const size_t xrow = static_cast<size_t>(C) * (BF16 ? 2 : 4);
+  // the channel this thread runs the conv of: q / k of the k-head, or v of a row
+  const bool fe_qk = tid < 2 * D;
+  const bool fe_v = tid < Sh::ROWS_WG;
+  const int ch_qk = tid < D ? kh * D + tid : A.Hk * D + kh * D + (tid - D);
+  const int ch_v = 2 * A.Hk * D + h * D + hb * Sh::ROWS_WG + tid;
+  const int chq = fe_qk ? ch_qk : 0, chv = fe_v ? ch_v : 0;  // clamped: every load stays in the row
 
-  const int slot = A.slot[b];
-  if (slot < 0 || slot >= A.n_slots) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) report_error(A.dev_err, GDN_DEV_BAD_SLOT);
-    return;
+  // ---- slot-independent inputs: token 0, conv weights, gates of token 0 ----
+  float xq = load_in<BF16>(xb, chq), xv = load_in<BF16>(xb, chv);
+  float4 wq = make_float4(0.f, 0.f, 0.f, 0.f), wv = wq;
+  if constexpr (W == 4) {
+    wq = *reinterpret_cast<const float4*>(A.conv_w + chq * 4);
+    wv = *reinterpret_cast<const float4*>(A.conv_w + chv * 4);
   }
+  size_t gi = static_cast<size_t>(b) * kdr * A.Hv + h;
+  float ga = load_in<BF16>(A.a, gi), gb = load_in<BF16>(A.b, gi);
 
-  // Issue the state loads first; nothing below waits on them until the row loop.
+  // A bad slot id is reported and its row skipped; the loads below then read
+  // slot 0 (harmless) so that no branch sits between the loads above and
+  // their use (a branch would let the compiler sink them behind the slot).
+  const bool slot_ok = slot_in >= 0 && slot_in < A.n_slots;
+  if (!slot_ok && tid == 0 && blockIdx.x == 0) report_error(A.dev_err, GDN_DEV_BAD_SLOT);
+  const int slot = slot_ok ? slot_in : 0;
+
+  // ---- the ring position, then the state rows (the position is requested
+  // first: loads complete in order, so the ring rows below wait for it alone) ----
+  const uint32_t pos = W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0u;
+  __builtin_amdgcn_sched_barrier(0);
   const float* Sg = A.state + (static_cast<size_t>(slot) * A.Hv + h) * D * D;
   f32x4_t S[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
     S[p] = load4(Sg + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4);
+  __builtin_amdgcn_sched_barrier(0);
 
-  const int R = A.R, C = A.C;
-  const float* ring = W > 0 ? A.conv_state + static_cast<size_t>(slot) * R * C : nullptr;
-  const uint32_t pos = W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0u;
-  const int kdr = VERIFY ? A.k : 1;
-  const void* xb = static_cast<const char*>(A.x) +
-                   static_cast<size_t>(b) * kdr * C * (BF16 ? 2 : 4);
-  const int cq = kh * D + c4;                         // q channels of this lane
-  const int ck = A.Hk * D + kh * D + c4;              // k channels of this lane
-  const int cv0 = 2 * A.Hk * D + h * D;               // v channels of this head
-  const bool qk_writer = (h % G == 0) && hb == 0 && wave == 0 && lane < LPR;
-  const bool v_writer = (lane % LPR) == 0;
+  // ---- conv window history of this thread's channels: ring rows pos-3 .. pos-1 ----
+  float hq[3] = {0.f, 0.f, 0.f}, hv[3] = {0.f, 0.f, 0.f};
+  if constexpr (W == 4) {
+    const float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
+    if constexpr (RING8) {
+      float rq[8], rv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        rq[r] = ring[static_cast<size_t>(r) * C + chq];
+        rv[r] = ring[static_cast<size_t>(r) * C + chv];
+      }
+      const uint32_t pu = __builtin_amdgcn_readfirstlane(pos);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const uint32_t r = (pu + static_cast<uint32_t>(t - 3)) & 7u;
+        float a = rq[0], c = rv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+          a = r == static_cast<uint32_t>(i) ? rq[i] : a;
+          c = r == static_cast<uint32_t>(i) ? rv[i] : c;
+        }
+        hq[t] = a;
+        hv[t] = c;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const float* rr = ring + static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(t - 3), R)) * C;
+        hq[t] = rr[chq];
+        hv[t] = rr[chv];
+      }
+    }
+  }
+  const bool qk_writer = fe_qk && (h % G == 0) && hb == 0 && slot_ok;
+  const bool v_writer = fe_v && slot_ok;
+  const bool o_writer = (lane % LPR) == 0 && slot_ok;
 
   for (int j = 0; j < kdr; ++j) {
-    // ---- front end: conv + SiLU, L2 norm of q and k, gates ----
-    float4 q = conv4<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, cq);
-    float4 k = conv4<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, ck);
-    float qs = A.q_scale, ks = 1.0f;
-    if (A.flags & GDN_FLAG_L2NORM_QK) {
-      const float sqq = group_sum<LPR>(dot4(q, q));
-      const float skk = group_sum<LPR>(dot4(k, k));
-      qs = qs * (1.0f / sqrtf(sqq + A.l2_eps));
-      ks = 1.0f / sqrtf(skk + A.l2_eps);
+    // next draft's inputs (verify), requested before this draft's arithmetic
+    float nxq = xq, nxv = xv, na = ga, nb = gb;
+    if (VERIFY && j + 1 < kdr) {
+      nxq = load_in<BF16>(xb + (j + 1) * xrow, chq);
+      nxv = load_in<BF16>(xb + (j + 1) * xrow, chv);
+      na = load_in<BF16>(A.a, gi + A.Hv);
+      nb = load_in<BF16>(A.b, gi + A.Hv);
     }
-    q = make_float4(q.x * qs, q.y * qs, q.z * qs, q.w * qs);
-    k = make_float4(k.x * ks, k.y * ks, k.z * ks, k.w * ks);
-    const float kq = group_sum<LPR>(dot4(k, q));
-    float v[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      v[p] = conv1<BF16, W>(ring, pos, R, xb, C, A.conv_w, j, cv0 + row0 + p * Sh::RPW);
-    const size_t gi = (static_cast<size_t>(b) * kdr + j) * A.Hv + h;
-    const float alpha = expf(-softplus_f(load_in<BF16>(A.a, gi)));
-    const float beta = sigmoid_f(load_in<BF16>(A.b, gi));
-
+    // ---- front end, one channel per thread: conv + SiLU, sums of squares ----
+    float* f = fe[j & 1];
+    float yq, yv;
+    if constexpr (W == 4) {
+      yq = silu_fast(fmaf(wq.w, xq, fmaf(wq.z, hq[2], fmaf(wq.y, hq[1], wq.x * hq[0]))));
+      yv = silu_fast(fmaf(wv.w, xv, fmaf(wv.z, hv[2], fmaf(wv.y, hv[1], wv.x * hv[0]))));
+      hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = xq;
+      hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = xv;
+    } else {
+      yq = xq;
+      yv = xv;
+    }
+    float sq = group_sum<NG < 32 ? NG : 32>(yq * yq);
+    if constexpr (NG == 64)  // the two 32-lane halves, added in a fixed order
+      sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sq), 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sq), 32));
+    if (fe_qk) {
+      f[tid] = yq;
+      if (tid % NG == 0) ssq[j & 1][tid / NG] = sq;
+    }
+    if (fe_v) f[2 * D + tid] = yv;
     // ---- append this token's raw input to the ring (rows nobody reads now) ----
     if constexpr (W > 0) {
       float* rrow = A.conv_state + (static_cast<size_t>(slot) * R + ring_row(pos + j, R)) * C;
-      if (qk_writer) {
-        *reinterpret_cast<float4*>(rrow + cq) = load_in4<BF16>(xb, static_cast<size_t>(j) * C + cq);
-        *reinterpret_cast<float4*>(rrow + ck) = load_in4<BF16>(xb, static_cast<size_t>(j) * C + ck);
-      }
-      if (v_writer) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int c = cv0 + row0 + p * Sh::RPW;
-          rrow[c] = load_in<BF16>(xb, static_cast<size_t>(j) * C + c);
-        }
-      }
+      if (qk_writer) rrow[chq] = xq;
+      if (v_writer) rrow[chv] = xv;
     }
+    lds_barrier();
+    if (!VERIFY && W > 0 && j == 0 && slot_ok && tid == 0) {
+      // Advance the position by this workgroup's share of one token.  Every
+      // wave of the workgroup has its position load completed (it picked its
+      // window rows before the barrier above); the shares of the slot's
+      // workgroups sum to exactly 1 << kPosShift and no partial sum reaches it,
+      // so every reader of this call sees the same position.
+      const uint32_t nwg = gridDim.x;
+      const uint32_t one = 1u << kPosShift;
+      const uint32_t share = one / nwg + (blockIdx.x < one % nwg ? 1u : 0u);
+      atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot), share);
+    }
+    // ---- L2 norm of q and k, gates ----
+    float sqq = 0.f, skk = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / NG; ++i) {
+      sqq += ssq[j & 1][i];
+      skk += ssq[j & 1][D / NG + i];
+    }
+    float qs = A.q_scale, ks = 1.0f;
+    if (A.flags & GDN_FLAG_L2NORM_QK) {
+      qs = qs * __builtin_amdgcn_rsqf(sqq + A.l2_eps);
+      ks = __builtin_amdgcn_rsqf(skk + A.l2_eps);
+    }
+    const float4 qr = *reinterpret_cast<const float4*>(f + c4);
+    const float4 kr = *reinterpret_cast<const float4*>(f + D + c4);
+    const float4 q = make_float4(qr.x * qs, qr.y * qs, qr.z * qs, qr.w * qs);
+    const float4 k = make_float4(kr.x * ks, kr.y * ks, kr.z * ks, kr.w * ks);
+    const float kq = group_sum<LPR>(dot4(k, q));
+    // alpha = exp(-softplus(a)) = 1 / (1 + e^a) = sigmoid(-a); beta = sigmoid(b)
+    const float alpha = sigmoid_fast(-ga);
+    const float beta = sigmoid_fast(gb);
 
     // ---- rank-1 delta update and output, one state row per lane group ----
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int row = row0 + p * Sh::RPW;
+      const float v = f[2 * D + rloc0 + p * Sh::RPW];
       const float sk = group_sum<LPR>(dot4v(S[p], k));
-      const float sq = group_sum<LPR>(dot4v(S[p], q));
-      const float u = beta * (v[p] - alpha * sk);
-      const float ov = fmaf(alpha, sq, u * kq);
+      const float sqv = group_sum<LPR>(dot4v(S[p], q));
+      const float u = beta * (v - alpha * sk);
+      const float ov = fmaf(alpha, sqv, u * kq);
       f32x4_t sn;
       sn.x = fmaf(u, k.x, alpha * S[p].x);
       sn.y = fmaf(u, k.y, alpha * S[p].y);
       sn.z = fmaf(u, k.z, alpha * S[p].z);
       sn.w = fmaf(u, k.w, alpha * S[p].w);
       S[p] = sn;
-      if (VERIFY) {
+      if (!VERIFY && slot_ok)
+        store_nt4(A.state + (static_cast<size_t>(slot) * A.Hv + h) * D * D + static_cast<size_t>(row) * D + c4, sn);
+      if (VERIFY && slot_ok) {
         float* dst = A.snap + ((((static_cast<size_t>(b) * kdr + j) * A.Hv + h) * D + row) * D + c4);
         store_nt4(dst, sn);
       }
-      if (v_writer) store_out<BF16>(A.o, (gi * D) + row, ov);
+      if (o_writer) store_out<BF16>(A.o, (gi * D) + row, ov);
     }
+    xq = nxq;
+    xv = nxv;
+    ga = na;
+    gb = nb;
+    gi += A.Hv;
   }
 
-  if (!VERIFY) {
-    float* Sw = A.state + (static_cast<size_t>(slot) * A.Hv + h) * D * D;
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      store_nt4(Sw + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4, S[p]);
-    if constexpr (W > 0) {
-      // Advance the position by this workgroup's share of one token; the
-      // shares of the slot's workgroups sum to exactly 1 << kPosShift, and
-      // no partial sum reaches it, so every reader of this call sees pos.
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const uint32_t nwg = gridDim.x;
-        const uint32_t one = 1u << kPosShift;
-        const uint32_t share = one / nwg + (blockIdx.x < one % nwg ? 1u : 0u);
-        atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot), share);
-      }
-    }
-  }
 }
 
 // Standalone conv-ring step over all C channels: y = SiLU(conv), append x.
@@ -312,8 +365,9 @@ template <int D, bool BF16, bool VERIFY>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
   using Sh = StepShape<D>;
   dim3 grid(a.Hv * Sh::WG_PER_HEAD, a.batch);
-  if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4>), grid, dim3(Sh::THREADS), 0, s, a);
-  else if (a.W == 0) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 0>), grid, dim3(Sh::THREADS), 0, s, a);
+  if (a.W == 4 && a.R == 8) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, true>), grid, dim3(Sh::THREADS), 0, s, a);
+  else if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, false>), grid, dim3(Sh::THREADS), 0, s, a);
+  else if (a.W == 0) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 0, false>), grid, dim3(Sh::THREADS), 0, s, a);
   else return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipGetLastError());
 }
