@@ -42,6 +42,7 @@
 // accumulators of tiles (2s, 2s+1) (bf16) or tile s (fp32) form exactly the
 // B operand that pairs with packed tile column s -- and, read the other way,
 // the packed A tile of the transposed product.
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -833,8 +834,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
 // ---------------------------------------------------------------------------
 // chain: sequential chunk loop, one wave per 16 rows of d_v
 // ---------------------------------------------------------------------------
-constexpr int kLoaders = 2;  // loader waves per chain workgroup
-
 template <int D, bool BF16, int CW>
 struct ChainSmem {
   using Gm = Geo<D, BF16>;
@@ -843,9 +842,12 @@ struct ChainSmem {
   static constexpr size_t VW = CW * 4 * Pk<BF16>::VC_BYTES;        // U' tiles of this workgroup's rows
   static constexpr size_t GATES = Gm::GATE_BYTES;
   static constexpr size_t BYTES = KQ + HT + VW + GATES;
-  // the loader waves copy whole rounds of kLoaders x 64 x 16 bytes
-  static constexpr size_t ROUND = kLoaders * 64 * 16;
-  static constexpr size_t BUF = (BYTES + ROUND - 1) / ROUND * ROUND;
+  // loader waves: 4 where every segment of the buffer is a multiple of 4 KB, else 2
+  static constexpr int NKQ = static_cast<int>(KQ / 1024), NHT = static_cast<int>(HT / 1024);
+  static constexpr int NVW = static_cast<int>(VW / 1024);
+  static constexpr int NL = (NKQ % 4 == 0 && NHT % 4 == 0 && NVW % 4 == 0) ? 4 : 2;
+  // 1 KB blocks: the segments above plus one block for the gates
+  static constexpr size_t BUF = static_cast<size_t>(NKQ + NHT + NVW + 1) * 1024;
   static_assert(2 * BUF <= 150 * 1024, "two chunk buffers must fit in LDS");
 };
 
@@ -866,7 +868,7 @@ __device__ __forceinline__ int chain_logical_index(int L, int nwg) {
 // waves of a workgroup sit on different SIMDs, so the copies cost the
 // compute waves no issue slots.
 template <int D, bool BF16, int CW>
-__global__ __launch_bounds__((CW + kLoaders) * 64, 1) void chain_kernel(PrefillArgs A, PrefillLayout Lay) {
+__global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void chain_kernel(PrefillArgs A, PrefillLayout Lay) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ChainSmem<D, BF16, CW>;
@@ -901,60 +903,68 @@ __global__ __launch_bounds__((CW + kLoaders) * 64, 1) void chain_kernel(PrefillA
   const int cr0 = c0 - first, ncl = c1 - c0;          // first chunk (within the sequence) and count
   float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
 
-  // ---- loader waves ----
+  // ---- loader waves: two chunks in flight in registers ----
   if (wave >= CW) {
+    constexpr int NL = Sm::NL;
     const int lw = wave - CW;
     const char* wsb = static_cast<const char*>(A.workspace);
     // 1 KB blocks [Q | -W, K^T, P | U' | gates]; loader lw copies blocks
-    // kLoaders j + lw.  Every segment starts at a multiple of kLoaders blocks,
-    // so the segment of round j is known at compile time.
-    constexpr int NKQ = static_cast<int>(Sm::KQ / 1024), NHT = static_cast<int>(Sm::HT / 1024);
-    constexpr int NVW = static_cast<int>(Sm::VW / 1024), NBLK = NKQ + NHT + NVW + 1;
-    constexpr int NJ = (NBLK + kLoaders - 1) / kLoaders;
-    static_assert(NKQ % kLoaders == 0 && NHT % kLoaders == 0 && NVW % kLoaders == 0 && Sm::VW % 1024 == 0,
-                  "segment alignment");
+    // NL j + lw.  Every segment starts at a multiple of NL blocks, so the
+    // segment of round j is known at compile time.
+    constexpr int NKQ = Sm::NKQ, NHT = Sm::NHT, NVW = Sm::NVW, NBLK = NKQ + NHT + NVW + 1;
+    constexpr int NJ = (NBLK + NL - 1) / NL;
+    static_assert(NKQ % NL == 0 && NHT % NL == 0 && NVW % NL == 0 && Sm::VW % 1024 == 0, "segment alignment");
     static_assert(Sm::GATES <= 1024, "gates fit one block");
-    auto load_chunk = [&](int chunk, char* base) {
+    static_assert(NBLK * 1024 == static_cast<int>(Sm::BUF), "blocks fill the buffer");
+    // Both register sets are always filled (a chunk past the end reloads the
+    // last chunk into unused registers), so their accesses stay unconditional.
+    const int clast = c0 + (ncl > 0 ? ncl - 1 : 0);
+    auto fetch = [&](uint4 (&r)[NJ], int chunk) {
+      chunk = min(chunk, clast);
       const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
       const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
       const char* vwb = hb + Gm::VW_OFF + static_cast<size_t>(zb) * CW * 4 * P::VC_BYTES;
-      // an opaque copy of this lane's offset: keeps the compiler from hoisting
-      // one address register per block out of the chunk loop, which would leave
-      // no registers for loads in flight
+      // an opaque copy of this lane's offset keeps the compiler from hoisting
+      // one address register per block out of the chunk loop
       int lo = lw * 1024 + lane * 16;
       asm volatile("" : "+v"(lo));
-      constexpr int NB = (NJ + 31) / 32, KB = (NJ + NB - 1) / NB;  // at most 32 loads in flight
 #pragma unroll
-      for (int bt = 0; bt < NB; ++bt) {
-        uint4 r[KB];
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-          const int j = bt * KB + k;
-          if (j >= NJ) break;
-          const int b0 = j * kLoaders;               // first block of this round
-          const char* src;
-          if (b0 < NKQ) src = kq + b0 * 1024;
-          else if (b0 < NKQ + NHT) src = hb + (b0 - NKQ) * 1024;
-          else if (b0 < NKQ + NHT + NVW) src = vwb + (b0 - NKQ - NHT) * 1024;
-          else src = hb + Gm::GATE_OFF - lw * 1024;  // gates: loader 0, lanes < GATES / 16
-          r[k] = (b0 + kLoaders <= NKQ + NHT + NVW || (lw == 0 && lane * 16 < static_cast<int>(Sm::GATES)))
-                     ? *reinterpret_cast<const uint4*>(src + lo)
-                     : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-          const int j = bt * KB + k;
-          if (j >= NJ) break;
-          *reinterpret_cast<uint4*>(base + j * kLoaders * 1024 + lo) = r[k];
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const int b0 = j * NL;                     // first block of this round
+        const char* src;
+        if (b0 < NKQ) src = kq + b0 * 1024;
+        else if (b0 < NKQ + NHT) src = hb + (b0 - NKQ) * 1024;
+        else if (b0 < NKQ + NHT + NVW) src = vwb + (b0 - NKQ - NHT) * 1024;
+        else src = hb + Gm::GATE_OFF - lw * 1024;  // gates: loader 0, lanes < GATES / 16
+        r[j] = (b0 + NL <= NKQ + NHT + NVW || (lw == 0 && lane * 16 < static_cast<int>(Sm::GATES)))
+                   ? *reinterpret_cast<const uint4*>(src + lo)
+                   : make_uint4(0, 0, 0, 0);
       }
     };
-    if (ncl > 0) load_chunk(c0, lds0);
+    auto put = [&](const uint4 (&r)[NJ], char* base) {
+      int lo = lw * 1024 + lane * 16;
+      asm volatile("" : "+v"(lo));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (j + 1 < NJ || lw == 0) *reinterpret_cast<uint4*>(base + j * NL * 1024 + lo) = r[j];
+    };
+    // Before barrier i the buffer (i % 2) holds chunk c0 + i; chunk i+1 and
+    // i+2 are in flight in the two register sets meanwhile.
+    uint4 ra[NJ], rb[NJ];
+    fetch(ra, c0);
+    fetch(rb, c0 + 1);
+    put(ra, lds0);
     lds_barrier();
-#pragma clang loop unroll(disable)
-    for (int ci = 0; ci < ncl; ++ci) {
-      if (ci + 1 < ncl) load_chunk(c0 + ci + 1, (ci & 1) ? lds0 : lds1);
+    fetch(ra, c0 + 2);
+    for (int ci = 0; ci < ncl; ci += 2) {
+      put(rb, lds1);            // chunk ci + 1 (past the end: never read)
       lds_barrier();
+      fetch(rb, c0 + ci + 3);
+      if (ci + 1 < ncl) {
+        put(ra, lds0);          // chunk ci + 2
+        lds_barrier();
+        fetch(ra, c0 + ci + 4);
+      }
     }
   } else {
 
@@ -1127,7 +1137,7 @@ __global__ __launch_bounds__((CW + kLoaders) * 64, 1) void chain_kernel(PrefillA
       }
     };
     if (h % G == 0 && zb == 0)
-      for (int cc = tid; cc < 2 * D; cc += (CW + kLoaders) * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
+      for (int cc = tid; cc < 2 * D; cc += (CW + Sm::NL) * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
     if (wave < CW && lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
     if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
   }
@@ -1142,13 +1152,52 @@ __global__ __launch_bounds__((CW + kLoaders) * 64, 1) void chain_kernel(PrefillA
 // kernel that reads it.
 constexpr int kSegChunks = 16;
 
+// The chain of segment k runs on a second stream of the library while the
+// chunk kernel of segment k+1 runs on the caller's stream: the two use
+// different compute units (the chain is latency-bound on a fraction of the
+// chip, the chunk kernel fills the rest).  One auxiliary stream and a few
+// events per device are created on the first prefill call on that device and
+// kept for the life of the process; the call joins the auxiliary stream back
+// into the caller's stream before it returns, so the caller sees every
+// kernel of the call ordered on its own stream (also under graph capture).
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[8] = {};
+};
+static std::mutex g_aux_mu;
+static AuxStream g_aux[64];
+
+static int aux_stream(AuxStream** out) {
+  int dev = 0;
+  int e = static_cast<int>(hipGetDevice(&dev));
+  if (e) return e;
+  if (dev < 0 || dev >= 64) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  AuxStream& x = g_aux[dev];
+  if (!x.s) {
+    hipStream_t st = nullptr;
+    e = static_cast<int>(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    if (e) return e;
+    for (hipEvent_t& ev : x.ev) {
+      e = static_cast<int>(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+      if (e) return e;
+    }
+    x.s = st;
+  }
+  *out = &x;
+  return 0;
+}
+
 template <int D, bool BF16>
 static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
   constexpr int CWMAX = BF16 ? 4 : 2;
   constexpr int CW = Geo<D, BF16>::NT < CWMAX ? Geo<D, BF16>::NT : CWMAX;
   const PrefillLayout L = layout_t<D, BF16>(a0.Hk, a0.Hv, a0.max_chunks, a0.n_seqs);
+  AuxStream* aux = nullptr;
+  int e = aux_stream(&aux);
+  if (e) return e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L);
-  int e = static_cast<int>(hipGetLastError());
+  e = static_cast<int>(hipGetLastError());
   if (e) return e;
   const size_t smem = ChunkSmem<D, BF16>::BYTES;
   auto chunk_fn = a0.W == 4 ? &chunk_kernel<D, BF16, 4> : &chunk_kernel<D, BF16, 0>;
@@ -1156,7 +1205,8 @@ static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
   if (e) return e;
   // at least one segment, so that sequences without tokens still get their slot written
-  for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks) {
+  int seg = 0;
+  for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks, ++seg) {
     PrefillArgs a = a0;
     a.seg_lo = lo;
     a.seg_hi = lo + kSegChunks;
@@ -1166,12 +1216,21 @@ static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
       e = static_cast<int>(hipGetLastError());
       if (e) return e;
     }
+    // the chain of this segment waits for its chunk kernel (and, through the
+    // caller's stream order, for the plan and every earlier chunk kernel)
+    hipEvent_t ready = aux->ev[1 + seg % 6];
+    e = static_cast<int>(hipEventRecord(ready, st));
+    if (e) return e;
+    e = static_cast<int>(hipStreamWaitEvent(aux->s, ready, 0));
+    if (e) return e;
     hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(a.n_seqs * a.Hv * (Geo<D, BF16>::NT / CW)),
-                       dim3((CW + kLoaders) * 64), 0, st, a, L);
+                       dim3((CW + ChainSmem<D, BF16, CW>::NL) * 64), 0, aux->s, a, L);
     e = static_cast<int>(hipGetLastError());
     if (e) return e;
   }
-  return 0;
+  e = static_cast<int>(hipEventRecord(aux->ev[7], aux->s));
+  if (e) return e;
+  return static_cast<int>(hipStreamWaitEvent(st, aux->ev[7], 0));
 }
 
 template <int D, bool BF16>
