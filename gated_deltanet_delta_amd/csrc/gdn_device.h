@@ -99,9 +99,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// SiLU and sigmoid with the hardware exp and reciprocal (about 2 ulp).
+// SiLU and sigmoid with the hardware exp2 and reciprocal (about 2 ulp).  An
+// argument so negative that 2^x underflows gives 1 + 0; so positive that it
+// overflows gives rcp(inf) = 0.
 __device__ __forceinline__ float sigmoid_fast(float y) {
-  return __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * y));
 }
 __device__ __forceinline__ float silu_fast(float y) {
   return y * sigmoid_fast(y);

@@ -90,7 +90,11 @@ struct Geo {
   static constexpr size_t HEAD_BYTES = VB_OFF + NT * 4 * P::VC_BYTES;
 };
 
-int prefill_max_chunks(int n_tokens, int n_seqs) { return (n_tokens + kC - 1) / kC + n_seqs; }
+// Sequence s needs ceil(len_s / C) chunks, and the sum of those is at most
+// floor((n_tokens + (C - 1) n_seqs) / C).
+int prefill_max_chunks(int n_tokens, int n_seqs) {
+  return static_cast<int>((static_cast<int64_t>(n_tokens) + static_cast<int64_t>(kC - 1) * n_seqs) / kC);
+}
 
 template <int D, bool BF16>
 static PrefillLayout layout_t(int Hk, int Hv, int maxc, int S) {
@@ -255,7 +259,7 @@ __device__ __forceinline__ void store16(float* d, int ld, f32x4_t v, float sign,
 // (lane = block x column), then the off-diagonal blocks level by level with
 // fp32 MFMA:  [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1].
 // tmp: 32 x 33 floats of scratch.
-__device__ void invert_unit_lower64(float* Lt, float* tmp, int lane) {
+__device__ __forceinline__ void invert_unit_lower64(float* Lt, float* tmp, int lane) {
   {
     const int bi = lane >> 4, c = lane & 15;
     float* Lb = Lt + 16 * bi * kLd + 16 * bi;
@@ -335,7 +339,8 @@ __device__ __forceinline__ uint4 pack_lane(F f) {
 // chunk: front end, gates, K K^T / K Q^T, then per v-head P, T, W and U'
 // (8 waves)
 // ---------------------------------------------------------------------------
-constexpr int kChunkThreads = 640;  // 10 waves: one conv item per thread at G = 3, d = 128
+// 12 waves: the 640 conv items at G = 3, d = 128 spread evenly over the 4 SIMDs
+constexpr int kChunkThreads = 768;
 constexpr int kChunkWaves = kChunkThreads / 64;
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
@@ -430,6 +435,17 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     return cc < D ? kh * D + cc : (cc < 2 * D ? Hk * D + kh * D + (cc - D) : 2 * Hk * D + kh * G * D + (cc - 2 * D));
   };
 
+  // gate inputs of the v-head whose gates this wave computes (the last G
+  // waves, one head each), loaded before the conv so they arrive under it
+  static_assert(kMaxGroup <= kChunkWaves, "one gate head per wave");
+  const int ghi = kChunkWaves - 1 - wave;
+  float a_in = 0.f, b_in = 0.f;
+  if (ghi < G && lane < len) {
+    const size_t i = static_cast<size_t>(t0 + lane) * Hv + kh * G + ghi;
+    a_in = load_in<BF16>(A.a, i);
+    b_in = load_in<BF16>(A.b, i);
+  }
+
   // ---- conv + SiLU: item = (VE channels, 16 tokens), the 19-row window in registers.
   // q|k items first, then v items; each wave takes a contiguous run of items. ----
   {
@@ -452,12 +468,21 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       const int c0 = xchan(cc0);
       const int tq = 16 * q;                        // first token of this quarter
       // raw rows: tokens t0+tq-3 .. t0+tq+15 (row i <-> token t0+tq-3+i),
-      // clamped into the sequence and the chunk so every load is valid
+      // clamped into the sequence and the chunk so every load is valid; an
+      // interior quarter needs no clamping, so its row addresses are one
+      // stride apart
       RawT raw[19];
+      const int tfirst = t0 + tq - 3;
+      if (tfirst >= seq_start && tq + 16 <= len) {
+        const E* xr = x + static_cast<size_t>(tfirst) * C + c0;
 #pragma unroll
-      for (int i = 0; i < 19; ++i) {
-        const int t = min(max(t0 + tq - 3 + i, seq_start), t0 + len - 1);
-        raw[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
+        for (int i = 0; i < 19; ++i) raw[i] = *reinterpret_cast<const RawT*>(xr + static_cast<size_t>(i) * C);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 19; ++i) {
+          const int t = min(max(tfirst + i, seq_start), t0 + len - 1);
+          raw[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
+        }
       }
       float w[VE][4];
       if constexpr (KW == 4) {
@@ -498,63 +523,67 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       const int hv = is_v ? (cc0 - 2 * D) / D : 0;  // v-head within the group
       const int dv0 = is_v ? (cc0 - 2 * D) % D : 0;
       E* vcb = reinterpret_cast<E*>(headb(kh * G + hv) + Gm::VB_OFF);
+      // tokens past the end of a ragged chunk give zero rows
+      auto run = [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {              // 4 groups of 4 tokens
-        float y[VE][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g4 + i;                 // token within the quarter
-          const bool valid = tq + r < len;
-#pragma unroll
-          for (int v = 0; v < VE; ++v) {
-            const float xin = elem(raw[3 + r], v);
-            float yy;
-            if constexpr (KW == 4) {
-              float acc = w[v][0] * hist[v][0];
-              acc = fmaf(w[v][1], hist[v][1], acc);
-              acc = fmaf(w[v][2], hist[v][2], acc);
-              acc = fmaf(w[v][3], xin, acc);
-              yy = silu_fast(acc);
-              hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
-            } else {
-              yy = xin;
-            }
-            y[v][i] = valid ? yy : 0.f;
-          }
-        }
-        if (!is_v) {
+        for (int g4 = 0; g4 < 4; ++g4) {              // 4 groups of 4 tokens
+          float y[VE][4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float* dst = qk + (tq + 4 * g4 + i) * QK_LD + cc0;
+            const int r = 4 * g4 + i;                 // token within the quarter
 #pragma unroll
-            for (int v = 0; v < VE; v += 4)
-              *reinterpret_cast<float4*>(dst + v) = make_float4(y[v][i], y[v + 1][i], y[v + 2][i], y[v + 3][i]);
+            for (int v = 0; v < VE; ++v) {
+              const float xin = elem(raw[3 + r], v);
+              float yy;
+              if constexpr (KW == 4) {
+                float acc = w[v][0] * hist[v][0];
+                acc = fmaf(w[v][1], hist[v][1], acc);
+                acc = fmaf(w[v][2], hist[v][2], acc);
+                acc = fmaf(w[v][3], xin, acc);
+                yy = silu_fast(acc);
+                hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
+              } else {
+                yy = xin;
+              }
+              y[v][i] = (FULL || tq + r < len) ? yy : 0.f;
+            }
           }
-        } else {
-          // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i
+          if (!is_v) {
 #pragma unroll
-          for (int v = 0; v < VE; ++v) {
-            const int dv = dv0 + v;
-            E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
-            if constexpr (BF16) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(y[v][0], y[v][1]), pack2_bf16(y[v][2], y[v][3]));
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
+            for (int i = 0; i < 4; ++i) {
+              float* dst = qk + (tq + 4 * g4 + i) * QK_LD + cc0;
+#pragma unroll
+              for (int v = 0; v < VE; v += 4)
+                *reinterpret_cast<float4*>(dst + v) = make_float4(y[v][i], y[v + 1][i], y[v + 2][i], y[v + 3][i]);
+            }
+          } else {
+            // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i
+#pragma unroll
+            for (int v = 0; v < VE; ++v) {
+              const int dv = dv0 + v;
+              E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
+              if constexpr (BF16) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(y[v][0], y[v][1]), pack2_bf16(y[v][2], y[v][3]));
+              } else {
+                *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
+              }
             }
           }
         }
-      }
+      };
+      if (tq + 16 <= len) run(std::true_type{});
+      else run(std::false_type{});
     }
   }
 
   // ---- gates: one wave per v-head (the last waves), lane = token, fixed-order inclusive scan ----
-  for (int hi = kChunkWaves - 1 - wave; hi >= 0 && hi < G; hi += kChunkWaves) {
-    const int h = kh * G + hi;
+  if (ghi < G) {
+    const int hi = ghi, h = kh * G + hi;
     float g = 0.f, bb = 0.f;
     if (lane < len) {
-      const size_t i = static_cast<size_t>(t0 + lane) * Hv + h;
-      g = -softplus_f(load_in<BF16>(A.a, i));
-      bb = sigmoid_f(load_in<BF16>(A.b, i));
+      g = -softplus_f(a_in);
+      bb = sigmoid_f(b_in);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -646,29 +675,64 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   __syncthreads();
 
   // ---- K K^T (lower 16x16 tiles) into LDS; K Q^T read as packed P tiles of
-  // every v-head (workspace) ----
+  // every v-head (workspace).  With a single inverse group the P tasks run on
+  // the waves the inverse leaves idle. ----
+  constexpr int NPT = TriTiles<BF16>::count();
+  const uint4* kh_t = pk;
+  const uint4* kl_t = pk + 4 * KSD * 64;
+  const uint4* q_t = pk + Sm::PK_Q * 4 * KSD * 64;
+  auto p_task = [&](int pt) {
+    int ti, ks;
+    TriTiles<BF16>::at(pt, ti, ks);
+    // (K Q^T)[j][r] with j = 16 tj + 4g + i, r = 16 ti + (lane & 15): the
+    // accumulator of tile (tj, ti) is packed P tile (ti, ks) element (tj%TPS)*4 + i
+    f32x4_t acc[TPS];
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+      const int tj = TPS * ks + u;
+      acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti) {
+#pragma unroll
+        for (int kd = 0; kd < KSD; ++kd)
+          acc[u] = Ch::step(kh_t[(tj * KSD + kd) * 64 + lane],
+                            __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]), acc[u]);
+      }
+    }
+    const int r = 16 * ti + (lane & 15), g = lane >> 4;
+    for (int hi = 0; hi < G; ++hi) {
+      const float* gc = gcum + hi * kC;
+      const float gr = gc[r];
+      float pv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
+      }
+      reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes)[lane] = pack(pv);
+    }
+  };
+  const bool p_later = G <= NH;
   {
-    constexpr int NPT = TriTiles<BF16>::count();
-    const uint4* kh_t = pk;
-    const uint4* kl_t = pk + 4 * KSD * 64;
-    const uint4* q_t = pk + Sm::PK_Q * 4 * KSD * 64;
-    for (int task = wave; task < 10 + NPT; task += kChunkWaves) {
+    const int ntask = p_later ? 10 : 10 + NPT;
+    for (int task = wave; task < ntask; task += kChunkWaves) {
       if (task < 10) {
         int t = task, ti = 0;
         while (t > ti) { t -= ti + 1; ++ti; }
         const int tj = t;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about fp32
+        // accuracy, in three independent accumulators
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           const uint4 ah = kh_t[(ti * KSD + ks) * 64 + lane];
           const Bop bh = __builtin_bit_cast(Bop, kh_t[(tj * KSD + ks) * 64 + lane]);
           acc = Ch::step(ah, bh, acc);
           if constexpr (BF16) {
-            // K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about fp32 accuracy
-            acc = Ch::step(ah, __builtin_bit_cast(Bop, kl_t[(tj * KSD + ks) * 64 + lane]), acc);
-            acc = Ch::step(kl_t[(ti * KSD + ks) * 64 + lane], bh, acc);
+            acc1 = Ch::step(ah, __builtin_bit_cast(Bop, kl_t[(tj * KSD + ks) * 64 + lane]), acc1);
+            acc2 = Ch::step(kl_t[(ti * KSD + ks) * 64 + lane], bh, acc2);
           }
         }
+        if constexpr (BF16) acc = acc + (acc1 + acc2);
         const int g = lane >> 4, j = 16 * tj + (lane & 15);
         if (G <= NH) {
           // one inverse group: L_rj = beta_r e^{G_r - G_j} (k_r . k_j), r > j, of every
@@ -690,34 +754,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
           for (int i = 0; i < 4; ++i) Am[(ti * 16 + g * 4 + i) * kLd + j] = acc[i];
         }
       } else {
-        int ti, ks;
-        TriTiles<BF16>::at(task - 10, ti, ks);
-        // (K Q^T)[j][r] with j = 16 tj + 4g + i, r = 16 ti + (lane & 15): the
-        // accumulator of tile (tj, ti) is packed P tile (ti, ks) element (tj%TPS)*4 + i
-        f32x4_t acc[TPS];
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-          const int tj = TPS * ks + u;
-          acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (tj <= ti) {
-#pragma unroll
-            for (int kd = 0; kd < KSD; ++kd)
-              acc[u] = Ch::step(kh_t[(tj * KSD + kd) * 64 + lane],
-                                __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]), acc[u]);
-          }
-        }
-        const int r = 16 * ti + (lane & 15), g = lane >> 4;
-        for (int hi = 0; hi < G; ++hi) {
-          const float* gc = gcum + hi * kC;
-          const float gr = gc[r];
-          float pv[EPL];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
-            pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
-          }
-          reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes)[lane] = pack(pv);
-        }
+        p_task(task - 10);
       }
     }
   }
@@ -726,6 +763,29 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   // ---- per group of NH v-heads: L, T = (I + L)^{-1}, then -W and U' ----
   for (int hg0 = 0; hg0 < G; hg0 += NH) {
     const int nh = min(NH, G - hg0);
+    // U' = T diag(beta) V: task (head, dvt) makes the 4 token tiles of 16
+    // columns.  The V tiles come from the workspace (L2): every wave
+    // issues the loads of all its U' tasks before the inverse, so they are
+    // in flight through the inverse, the T packing and the -W tasks.
+    constexpr int MAXV = (NH * NT + kChunkWaves - 1) / kChunkWaves;
+    const int nv = nh * NT;
+    Bop vop[MAXV][KSC];
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int t = min(wave + k * kChunkWaves, nv - 1);  // a clamped duplicate is loaded, never used
+      const int i = t / NT, dvt = t % NT;
+      const E* vb = reinterpret_cast<const E*>(headb(kh * G + hg0 + i) + Gm::VB_OFF) + dvt * 4 * 256 + lane * 4;
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        if constexpr (BF16) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vb + (2 * ks) * 256);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vb + (2 * ks + 1) * 256);
+          vop[k][ks] = __builtin_bit_cast(Bop, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          vop[k][ks] = __builtin_bit_cast(Bop, *reinterpret_cast<const uint4*>(vb + ks * 256));
+        }
+      }
+    }
     if (G > NH) {  // several groups: L of this group from K K^T in LDS
       for (int e = tid; e < nh * kC * kC; e += kChunkThreads) {
         const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
@@ -734,7 +794,11 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       }
       __syncthreads();
     }
-    if (wave < nh) invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
+    if (wave < nh) {
+      invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
+    } else if (p_later) {
+      for (int pt = wave - nh; pt < NPT; pt += kChunkWaves - nh) p_task(pt);
+    }
     __syncthreads();
     // T diag(beta e^G) (for W) and T diag(beta) (for U') as A tiles; the
     // identically zero tiles above the diagonal are never read
@@ -755,29 +819,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       tt[((i * 2 + which) * 4 * KSC + tile) * 64 + ln] = pack(tv);
     }
     __syncthreads();
-    // U' = T diag(beta) V: task (head, dvt) makes the 4 token tiles of 16
-    // columns.  The V tiles come from the workspace (L2), so every wave
-    // issues the loads of all its U' tasks first and runs its -W tasks
-    // (operands in LDS) while they are in flight.
-    constexpr int MAXV = (NH * NT + kChunkWaves - 1) / kChunkWaves;
-    const int nv = nh * NT;
-    Bop vop[MAXV][KSC];
-#pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
-      const int t = min(wave + k * kChunkWaves, nv - 1);  // a clamped duplicate is loaded, never used
-      const int i = t / NT, dvt = t % NT;
-      const E* vb = reinterpret_cast<const E*>(headb(kh * G + hg0 + i) + Gm::VB_OFF) + dvt * 4 * 256 + lane * 4;
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        if constexpr (BF16) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vb + (2 * ks) * 256);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vb + (2 * ks + 1) * 256);
-          vop[k][ks] = __builtin_bit_cast(Bop, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        } else {
-          vop[k][ks] = __builtin_bit_cast(Bop, *reinterpret_cast<const uint4*>(vb + ks * 256));
-        }
-      }
-    }
     // -W = -(T diag(beta e^G)) K: W^T = K^T (T diag(beta e^G))^T, tile (dt, mt)
     // accumulators read as packed A tile (mt, ksd) of W (rows token, k = d)
     const int nw = nh * 4 * KSD;

@@ -115,6 +115,19 @@ def test_prefill_varlen_ragged_with_empty_and_init():
     _check(g, inp, pool, o)
 
 
+@pytest.mark.parametrize("lengths", [[65] * 9, [1] * 20, [1, 65, 129, 193, 1, 65, 129, 257]])
+def test_prefill_chunk_count_at_its_bound(lengths):
+    """Partitions whose chunk count equals the workspace bound
+    floor((n_tokens + 63 n_seqs) / 64), across the 16-chunk launch segments."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=2, n_slots=len(lengths))
+    inp = gi.prefill_inputs(seed=400 + len(lengths), geom=g, lengths=lengths, init_state=True, a_mean=-2.0)
+    n = sum(lengths)
+    assert sum((t + 63) // 64 for t in lengths) == (n + 63 * len(lengths)) // 64
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o)
+
+
 def test_prefill_then_decode_continues_the_sequence():
     """Prefill the first part of a sequence, decode the rest token by token:
     matches the oracle over the whole sequence."""
