@@ -123,6 +123,28 @@ __device__ __forceinline__ int ring_row(uint32_t p, int R) { return static_cast<
 __device__ __forceinline__ void store_nt4(float* p, f32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
+// Stores that write through this XCD's L2 to memory: relaxed agent-scope
+// atomic stores, which the compiler emits as plain vector stores with the
+// sc1 policy (no fence).  Data a concurrently running kernel on another XCD
+// reads goes out this way, so publishing it needs only the wave's own store
+// counter (wait_stores), not a write-back of the whole L2.
+__device__ __forceinline__ void store_wt(void* p, uint2 v) {
+  const uint64_t w = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_wt(void* p, uint4 v) {
+  store_wt(p, make_uint2(v.x, v.y));
+  store_wt(static_cast<char*>(p) + 8, make_uint2(v.z, v.w));
+}
+__device__ __forceinline__ void store_wt(void* p, float4 v) {
+  store_wt(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+__device__ __forceinline__ void store_wt(void* p, float v) {
+  __hip_atomic_store(reinterpret_cast<float*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access this wave issued has completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ f32x4_t load4(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }

@@ -48,13 +48,15 @@ struct PrefillArgs {
   uint32_t flags;
   float q_scale, l2_eps;
   int32_t seg_lo, seg_hi;  // chunk-table range of one launch segment (set by the launcher)
+  int32_t persistent;      // 1: one chain launch over whole sequences, waiting on per-chunk ready flags
 };
 
 // Byte offsets and block sizes of the prefill workspace.
 //   kq:   per (chunk, k-head) block of packed Q operand tiles (kq_bytes each)
 //   head: per (chunk, v-head) block of packed -W, decayed K^T, P, U', the gate factors and V (head_bytes each)
+//   ready: per (chunk, k-head) flag, set once the chunk kernel has published that block
 struct PrefillLayout {
-  size_t kq, head, chunk_tab, seq_tab, counters, total;
+  size_t kq, head, chunk_tab, seq_tab, counters, ready, total;
   size_t kq_bytes, head_bytes;
 };
 PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int max_chunks, int n_seqs);

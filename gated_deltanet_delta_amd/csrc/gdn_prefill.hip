@@ -110,6 +110,7 @@ static PrefillLayout layout_t(int Hk, int Hv, int maxc, int S) {
   L.chunk_tab = take(mc * 4 * 4);
   L.seq_tab = take(static_cast<size_t>(S) * 8 * 4);
   L.counters = take(256);
+  L.ready = take(mc * Hk * 4);
   L.total = off;
   return L;
 }
@@ -174,6 +175,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
     cnt[0] = total;
     s_total = total;
   }
+  // every (chunk, k-head) starts unpublished
+  int32_t* ready = ws_ptr<int32_t>(A.workspace, L.ready);
+  for (int i = threadIdx.x; i < A.max_chunks * A.Hk; i += blockDim.x) ready[i] = 0;
   __syncthreads();
   const int total = s_total;
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
@@ -413,8 +417,10 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   float* bge = dkf + kMaxGroup * kC;                       // [8][64] beta e^G
   float* inv = bge + kMaxGroup * kC;                       // [2][64] q and k norm factors
 
-  const int chunk = A.seg_lo + blockIdx.x;
-  const int kh = blockIdx.y;
+  // grid (k-heads, chunks): workgroups are dispatched chunk by chunk, the
+  // order in which the chain kernel consumes them
+  const int chunk = A.seg_lo + blockIdx.y;
+  const int kh = blockIdx.x;
   const int n_chunks = ws_ptr<int32_t>(A.workspace, Lay.counters)[0];
   if (chunk >= n_chunks) return;
   const int32_t* ce = ws_ptr<int32_t>(A.workspace, Lay.chunk_tab) + 4 * chunk;
@@ -597,8 +603,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     dkf[hi * kC + lane] = __expf(glast - g);
     bge[hi * kC + lane] = bb * eg;
     float* gw = reinterpret_cast<float*>(headb(h) + Gm::GATE_OFF);
-    gw[lane] = eg;
-    gw[kC + lane] = __expf(glast);
+    store_wt(gw + lane, eg);
+    store_wt(gw + kC + lane, __expf(glast));
   }
 
   __syncthreads();
@@ -646,7 +652,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       qv[e] = k < D ? qn(row, k) : 0.f;
     }
     const uint4 qw = pack(qv);
-    reinterpret_cast<uint4*>(kqb)[tile * 64 + ln] = qw;
+    store_wt(reinterpret_cast<uint4*>(kqb) + tile * 64 + ln, qw);
     pk[(Sm::PK_Q * 4 * KSD + tile) * 64 + ln] = qw;
     pk[tile * 64 + ln] = pack(kv);
     if constexpr (BF16) {
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       float dv[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dv[e] = kv[e] * dk_h[ks * SK + (e >> 2) * 16 + 4 * g + (e & 3)];
-      reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::KDA + tile) * kTileBytes)[ln] = pack(dv);
+      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::KDA + tile) * kTileBytes) + ln, pack(dv));
     }
   }
   __syncthreads();
@@ -708,7 +714,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
         const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
         pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
       }
-      reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes)[lane] = pack(pv);
+      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes) + lane, pack(pv));
     }
   };
   const bool p_later = G <= NH;
@@ -842,7 +848,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       float wv[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) wv[e] = -acc[e >> 2][e & 3];
-      reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::WA + mt * KSD + ksd) * kTileBytes)[lane] = pack(wv);
+      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::WA + mt * KSD + ksd) * kTileBytes) + lane, pack(wv));
     }
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
@@ -861,20 +867,35 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
             uint2 pkd;
             pkd.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
             pkd.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[3])) << 16);
-            *reinterpret_cast<uint2*>(vw + mt * 256) = pkd;
+            store_wt(vw + mt * 256, pkd);
           } else {
-            *reinterpret_cast<float4*>(vw + mt * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            store_wt(vw + mt * 256, make_float4(acc[0], acc[1], acc[2], acc[3]));
           }
         }
       }
     }
     __syncthreads();  // Lt and the T tiles are reused by the next group
   }
+
+  // ---- publish (chunk, k-head) for a chain kernel running concurrently.
+  // Everything the chain reads went out with write-through stores; once
+  // every wave has seen its stores complete, the flag is set (itself a
+  // write-through store) ----
+  if (A.persistent) {
+    wait_stores();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(ws_ptr<int32_t>(A.workspace, Lay.ready) + chunk * Hk + kh, 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // chain: sequential chunk loop, one wave per 16 rows of d_v
 // ---------------------------------------------------------------------------
+// s_sleep(2) polls of a ready flag before a persistent chain gives up (about a second)
+constexpr int kReadySpins = 1 << 24;
+
 template <int D, bool BF16, int CW>
 struct ChainSmem {
   using Gm = Geo<D, BF16>;
@@ -960,8 +981,28 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
     // Both register sets are always filled (a chunk past the end reloads the
     // last chunk into unused registers), so their accesses stay unconditional.
     const int clast = c0 + (ncl > 0 ? ncl - 1 : 0);
+    // In a persistent launch the chunk kernel runs concurrently: wait until it
+    // has published (chunk, kh).  The flag is read with an agent-scope atomic
+    // (it bypasses this XCD's L2); the operand lines read after it were not
+    // touched earlier by this kernel, so they come from memory.  The wait is
+    // bounded: on time-out the error word is set and the loader goes on.
+    const int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
+    bool timed_out = false;
+    auto wait_ready = [&](int chunk) {
+      if (!A.persistent || timed_out) return;
+      const int32_t* f = ready + chunk * Hk + kh;
+      for (int spins = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kReadySpins) {
+          report_error(A.dev_err, GDN_DEV_WAIT_TIMEOUT);
+          timed_out = true;
+          break;
+        }
+      }
+    };
     auto fetch = [&](uint4 (&r)[NJ], int chunk) {
       chunk = min(chunk, clast);
+      wait_ready(chunk);
       const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
       const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
       const char* vwb = hb + Gm::VW_OFF + static_cast<size_t>(zb) * CW * 4 * P::VC_BYTES;
@@ -992,11 +1033,13 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
     // Before barrier i the buffer (i % 2) holds chunk c0 + i; chunk i+1 and
     // i+2 are in flight in the two register sets meanwhile.
     uint4 ra[NJ], rb[NJ];
-    fetch(ra, c0);
-    fetch(rb, c0 + 1);
-    put(ra, lds0);
+    if (ncl > 0) {  // a sequence without chunks stages nothing (its chunk index may be past the table)
+      fetch(ra, c0);
+      fetch(rb, c0 + 1);
+      put(ra, lds0);
+    }
     lds_barrier();
-    fetch(ra, c0 + 2);
+    if (ncl > 0) fetch(ra, c0 + 2);
     for (int ci = 0; ci < ncl; ci += 2) {
       put(rb, lds1);            // chunk ci + 1 (past the end: never read)
       lds_barrier();
@@ -1229,6 +1272,10 @@ static int aux_stream(AuxStream** out) {
   return 0;
 }
 
+// Largest chain grid that runs as one launch beside the chunk kernel (half the
+// CUs: the rest stay free for chunk workgroups, which never wait).
+constexpr int kPersistentChainMax = 128;
+
 template <int D, bool BF16>
 static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
   constexpr int CWMAX = BF16 ? 4 : 2;
@@ -1245,29 +1292,52 @@ static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
   e = static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
   if (e) return e;
-  // at least one segment, so that sequences without tokens still get their slot written
-  int seg = 0;
-  for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks, ++seg) {
+  const int chain_wgs = a0.n_seqs * a0.Hv * (Geo<D, BF16>::NT / CW);
+  const dim3 chain_block((CW + ChainSmem<D, BF16, CW>::NL) * 64);
+  if (chain_wgs <= kPersistentChainMax && a0.max_chunks <= 65535) {  // 65535: grid y limit
+    // One chain launch over whole sequences, beside one chunk launch over all
+    // chunks: the chain's loaders wait on each (chunk, k-head) flag.  The chain
+    // grid holds at most half the CUs, so chunk workgroups always find CUs.
     PrefillArgs a = a0;
-    a.seg_lo = lo;
-    a.seg_hi = lo + kSegChunks;
-    const int n = a0.max_chunks - lo < kSegChunks ? a0.max_chunks - lo : kSegChunks;
-    if (n > 0) {
-      hipLaunchKernelGGL(chunk_fn, dim3(n, a.Hk), dim3(kChunkThreads), smem, st, a, L);
+    a.persistent = 1;
+    a.seg_lo = 0;
+    a.seg_hi = a0.max_chunks;
+    e = static_cast<int>(hipEventRecord(aux->ev[0], st));  // after the plan
+    if (e) return e;
+    e = static_cast<int>(hipStreamWaitEvent(aux->s, aux->ev[0], 0));
+    if (e) return e;
+    hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(chain_wgs), chain_block, 0, aux->s, a, L);
+    e = static_cast<int>(hipGetLastError());
+    if (e) return e;
+    if (a0.max_chunks > 0) {
+      hipLaunchKernelGGL(chunk_fn, dim3(a.Hk, a0.max_chunks), dim3(kChunkThreads), smem, st, a, L);
       e = static_cast<int>(hipGetLastError());
       if (e) return e;
     }
-    // the chain of this segment waits for its chunk kernel (and, through the
-    // caller's stream order, for the plan and every earlier chunk kernel)
-    hipEvent_t ready = aux->ev[1 + seg % 6];
-    e = static_cast<int>(hipEventRecord(ready, st));
-    if (e) return e;
-    e = static_cast<int>(hipStreamWaitEvent(aux->s, ready, 0));
-    if (e) return e;
-    hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(a.n_seqs * a.Hv * (Geo<D, BF16>::NT / CW)),
-                       dim3((CW + ChainSmem<D, BF16, CW>::NL) * 64), 0, aux->s, a, L);
-    e = static_cast<int>(hipGetLastError());
-    if (e) return e;
+  } else {
+    // at least one segment, so that sequences without tokens still get their slot written
+    int seg = 0;
+    for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks, ++seg) {
+      PrefillArgs a = a0;
+      a.seg_lo = lo;
+      a.seg_hi = lo + kSegChunks;
+      const int n = a0.max_chunks - lo < kSegChunks ? a0.max_chunks - lo : kSegChunks;
+      if (n > 0) {
+        hipLaunchKernelGGL(chunk_fn, dim3(a.Hk, n), dim3(kChunkThreads), smem, st, a, L);
+        e = static_cast<int>(hipGetLastError());
+        if (e) return e;
+      }
+      // the chain of this segment waits for its chunk kernel (and, through the
+      // caller's stream order, for the plan and every earlier chunk kernel)
+      hipEvent_t ready = aux->ev[1 + seg % 6];
+      e = static_cast<int>(hipEventRecord(ready, st));
+      if (e) return e;
+      e = static_cast<int>(hipStreamWaitEvent(aux->s, ready, 0));
+      if (e) return e;
+      hipLaunchKernelGGL((chain_kernel<D, BF16, CW>), dim3(chain_wgs), chain_block, 0, aux->s, a, L);
+      e = static_cast<int>(hipGetLastError());
+      if (e) return e;
+    }
   }
   e = static_cast<int>(hipEventRecord(aux->ev[7], aux->s));
   if (e) return e;

@@ -96,6 +96,7 @@ typedef enum gdn_status {
 #define GDN_DEV_BAD_SLOT 1       /* slot id outside [0, n_slots) */
 #define GDN_DEV_BAD_ACCEPTED 2   /* accepted length outside [0, k] */
 #define GDN_DEV_BAD_SEQLENS 3    /* cu_seqlens[0] != 0, decreasing, or last != n_tokens */
+#define GDN_DEV_WAIT_TIMEOUT 4   /* prefill: a chunk's operands were not published in time; outputs invalid */
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 

@@ -18,7 +18,7 @@ def _gdn():
     return gdn
 
 
-def _prefill(g, inp, pool=None):
+def _prefill(g, inp, pool=None, ws=None):
     gdn = _gdn()
     geom = H.to_geom(g)
     dt = H.in_dtype(g)
@@ -27,7 +27,8 @@ def _prefill(g, inp, pool=None):
     N = inp["x"].shape[0]
     S = len(inp["cu_seqlens"]) - 1
     o = torch.zeros(N, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
-    ws = gdn.alloc_prefill_workspace(geom, N, S)
+    if ws is None:
+        ws = gdn.alloc_prefill_workspace(geom, N, S)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     gdn.prefill_chunked(geom, pool, H.dev(inp["x"], dt), H.dev(inp["a"], dt), H.dev(inp["b"], dt),
                         H.dev(inp["conv_w"]) if g.conv_width else None, H.dev(inp["cu_seqlens"]),
@@ -126,6 +127,41 @@ def test_prefill_chunk_count_at_its_bound(lengths):
     pool, o, err = _prefill(g, inp)
     assert err == 0
     _check(g, inp, pool, o)
+
+
+@pytest.mark.parametrize("lengths", [[65, 0], [0, 1, 0], [64, 64, 0, 0]])
+def test_prefill_trailing_empty_sequences(lengths):
+    """Empty sequences after the last chunk: their chunk index equals the
+    chunk-count bound, so nothing may be staged for them."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=2, n_slots=len(lengths))
+    inp = gi.prefill_inputs(seed=410 + len(lengths), geom=g, lengths=lengths, init_state=True, a_mean=-2.0)
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o)
+
+
+def test_prefill_reused_workspace_sees_new_inputs():
+    """Two different prefills back to back on one workspace: the second reads
+    only what its own chunk kernel published."""
+    gdn = _gdn()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=2)
+    inp1 = gi.prefill_inputs(seed=501, geom=g, lengths=[300])
+    inp2 = gi.prefill_inputs(seed=502, geom=g, lengths=[300])
+    ws = gdn.alloc_prefill_workspace(H.to_geom(g), 300, 1)
+    _prefill(g, inp1, ws=ws)
+    pool, o, err = _prefill(g, inp2, ws=ws)
+    assert err == 0
+    _check(g, inp2, pool, o)
+
+
+def test_prefill_segmented_launches():
+    """A chain grid above the single-launch limit (2 sequences x 48 v-heads x
+    2 column groups) runs as 16-chunk launch segments."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_slots=2)
+    inp = gi.prefill_inputs(seed=503, geom=g, lengths=[1100, 70], init_state=True, a_mean=-2.0)
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o, heads=[0, 13, 47])
 
 
 def test_prefill_then_decode_continues_the_sequence():
