@@ -123,24 +123,34 @@ __device__ __forceinline__ int ring_row(uint32_t p, int R) { return static_cast<
 __device__ __forceinline__ void store_nt4(float* p, f32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
-// Stores that write through this XCD's L2 to memory: relaxed agent-scope
-// atomic stores, which the compiler emits as plain vector stores with the
-// sc1 policy (no fence).  Data a concurrently running kernel on another XCD
-// reads goes out this way, so publishing it needs only the wave's own store
-// counter (wait_stores), not a write-back of the whole L2.
-__device__ __forceinline__ void store_wt(void* p, uint2 v) {
-  const uint64_t w = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Stores that write through this XCD's L2 to memory (cache policy sc1).
+// Data a concurrently running kernel on another XCD reads goes out this way,
+// so publishing it needs only the wave's own store counter (wait_stores), not
+// a write-back of the whole L2.  They are buffer stores: `base` is the same
+// in every lane of the wave (it becomes the buffer descriptor), `off` is the
+// lane's byte offset from it.
+constexpr int kStoreSc1 = 16;  // cache-policy operand of the buffer builtins: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  // raw buffer: stride 0, whole 2 GB range, 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                                           static_cast<short>(0), 0x7fffffff, 0x00020000);
 }
-__device__ __forceinline__ void store_wt(void* p, uint4 v) {
-  store_wt(p, make_uint2(v.x, v.y));
-  store_wt(static_cast<char*>(p) + 8, make_uint2(v.z, v.w));
+__device__ __forceinline__ void store_wt(const void* base, uint32_t off, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, wt_rsrc(base), off, 0, kStoreSc1);
 }
-__device__ __forceinline__ void store_wt(void* p, float4 v) {
-  store_wt(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+__device__ __forceinline__ void store_wt(const void* base, uint32_t off, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, wt_rsrc(base), off, 0, kStoreSc1);
 }
-__device__ __forceinline__ void store_wt(void* p, float v) {
-  __hip_atomic_store(reinterpret_cast<float*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_wt(const void* base, uint32_t off, float4 v) {
+  store_wt(base, off, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+__device__ __forceinline__ void store_wt(const void* base, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), wt_rsrc(base), off, 0, kStoreSc1);
 }
 // Wait until every vector memory access this wave issued has completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -603,8 +603,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     dkf[hi * kC + lane] = __expf(glast - g);
     bge[hi * kC + lane] = bb * eg;
     float* gw = reinterpret_cast<float*>(headb(h) + Gm::GATE_OFF);
-    store_wt(gw + lane, eg);
-    store_wt(gw + kC + lane, __expf(glast));
+    store_wt(gw, 4 * lane, eg);
+    store_wt(gw, 4 * (kC + lane), __expf(glast));
   }
 
   __syncthreads();
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       qv[e] = k < D ? qn(row, k) : 0.f;
     }
     const uint4 qw = pack(qv);
-    store_wt(reinterpret_cast<uint4*>(kqb) + tile * 64 + ln, qw);
+    store_wt(kqb, 16 * (tile * 64 + ln), qw);
     pk[(Sm::PK_Q * 4 * KSD + tile) * 64 + ln] = qw;
     pk[tile * 64 + ln] = pack(kv);
     if constexpr (BF16) {
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       float dv[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dv[e] = kv[e] * dk_h[ks * SK + (e >> 2) * 16 + 4 * g + (e & 3)];
-      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::KDA + tile) * kTileBytes) + ln, pack(dv));
+      store_wt(headb(kh * G + hi), (Gm::KDA + tile) * kTileBytes + 16 * ln, pack(dv));
     }
   }
   __syncthreads();
@@ -714,7 +714,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
         const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
         pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
       }
-      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hi) + (Gm::PA + ti * KSC + ks) * kTileBytes) + lane, pack(pv));
+      store_wt(headb(kh * G + hi), (Gm::PA + ti * KSC + ks) * kTileBytes + 16 * lane, pack(pv));
     }
   };
   const bool p_later = G <= NH;
@@ -848,7 +848,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       float wv[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) wv[e] = -acc[e >> 2][e & 3];
-      store_wt(reinterpret_cast<uint4*>(headb(kh * G + hg0 + i) + (Gm::WA + mt * KSD + ksd) * kTileBytes) + lane, pack(wv));
+      store_wt(headb(kh * G + hg0 + i), (Gm::WA + mt * KSD + ksd) * kTileBytes + 16 * lane, pack(wv));
     }
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
@@ -856,7 +856,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
       if (t < nv) {
         const int i = t / NT, dvt = t % NT;
         const uint4* tb = tt + (i * 2 + 1) * 4 * KSC * 64;
-        E* vw = reinterpret_cast<E*>(headb(kh * G + hg0 + i) + Gm::VW_OFF) + dvt * 4 * 256 + lane * 4;
+        char* hbv = headb(kh * G + hg0 + i);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -867,9 +867,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
             uint2 pkd;
             pkd.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
             pkd.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[3])) << 16);
-            store_wt(vw + mt * 256, pkd);
+            store_wt(hbv, Gm::VW_OFF + ((dvt * 4 + mt) * 256 + lane * 4) * sizeof(E), pkd);
           } else {
-            store_wt(vw + mt * 256, make_float4(acc[0], acc[1], acc[2], acc[3]));
+            store_wt(hbv, Gm::VW_OFF + ((dvt * 4 + mt) * 256 + lane * 4) * sizeof(E), make_float4(acc[0], acc[1], acc[2], acc[3]));
           }
         }
       }
