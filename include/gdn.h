@@ -188,6 +188,12 @@ gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_stat
  *   slot, has_init [n_seqs] int32 (device).
  *   workspace: device, >= gdn_prefill_workspace_bytes(g, n_tokens, n_seqs).
  *   1 <= n_seqs <= n_slots, 0 <= n_tokens.
+ * The call enqueues work on `stream` and on a library-owned stream of the
+ * current device; before it returns, `stream` is made to wait for all of it,
+ * so later work on `stream` sees the results.  Calls that share a workspace
+ * must be ordered on one stream.  *dev_err receives GDN_DEV_WAIT_TIMEOUT if
+ * the internal producer/consumer hand-off ever stalls (the outputs are then
+ * not valid).
  */
 gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_state,
                                int32_t* conv_pos, const void* x, const void* a, const void* b,
