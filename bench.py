@@ -48,11 +48,130 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=1024,
                    help="prefix of the prefill sequence the CPU oracle runs on")
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="run only the counter workload: a 1 GiB calibration copy, then two prefills")
+    p.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the prefill traffic summary from two rocprofv3 --pmc counter CSVs")
     return p.parse_args()
+
+
+# ---------------- HBM traffic from FETCH_SIZE / WRITE_SIZE counter runs ----------------
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic_T8192.md")
+TRAFFIC_SOURCES = ["gated_deltanet_delta_amd/csrc/gdn_prefill.hip", "gated_deltanet_delta_amd/csrc/gdn_device.h",
+                   "gated_deltanet_delta_amd/csrc/gdn_internal.h"]
+CALIB_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
+
+
+def prefill_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_probe():
+    """Counter workload: one calibration copy of known size, then two prefills
+    of the benchmark's sequence (the second one is the one summarised)."""
+    import torch
+    import gated_deltanet_delta_amd as gdn
+    import gdn_inputs as gi
+    gdn.lib()
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = gi.GEOM_QWEN
+    geom = gdn.Geometry()
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)  # reads and writes CALIB_BYTES
+    torch.cuda.synchronize()
+    del src, dst
+    pin = gi.workload(3)
+    args = [torch.from_numpy(pin[k]).to(bf).to(dev) for k in ("x", "a", "b")]
+    cw = torch.from_numpy(pin["conv_w"]).to(dev)
+    cu = torch.from_numpy(pin["cu_seqlens"]).to(dev)
+    sl = torch.from_numpy(pin["slots"]).to(dev)
+    hi = torch.from_numpy(pin["has_init"]).to(dev)
+    pool = gdn.SlotPool.zeros(geom)
+    o = torch.empty(T_PREFILL, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    ws = gdn.alloc_prefill_workspace(geom, T_PREFILL, 1)
+    for _ in range(2):
+        gdn.prefill_chunked(geom, pool, *args, cw, cu, sl, hi, o, ws)
+        torch.cuda.synchronize()
+    print("pmc probe done", flush=True)
+
+
+def pmc_read(path, counter):
+    """Per-dispatch (dispatch id, kernel name, value) of one counter, in dispatch order."""
+    import csv
+    vals = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = vals.get(d, (r["Kernel_Name"], 0.0))
+            vals[d] = (name, v + float(r["Counter_Value"]))
+    return [(d,) + vals[d] for d in sorted(vals)]
+
+
+def pmc_summarize(fetch_csv, write_csv):
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = pmc_read(path, counter)
+        calib = max((r for r in rows if "elementwise" in r[1]), key=lambda r: r[2])
+        plans = [i for i, r in enumerate(rows) if "plan_kernel" in r[1]]
+        last = [r for r in rows[plans[-1]:] if "gdn::" in r[1]]
+        factor = CALIB_BYTES / (calib[2] * 1024.0)  # counter reads KiB
+        per_kernel = {}
+        for _, name, v in last:
+            key = name.split("(")[0]
+            per_kernel[key] = per_kernel.get(key, 0.0) + v * 1024.0 * factor
+        out[counter] = (calib[2], factor, per_kernel)
+    total = sum(sum(pk.values()) for _, _, pk in out.values())
+    lines = ["# Prefill HBM traffic, T = 8192 (16 k-heads, 48 v-heads, d = 128, bf16)", "",
+             "Commands (from /tmp, TMPDIR=/tmp), one counter per run:", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d <dir_f> -o f --output-format csv -- python3 bench.py --pmc-probe",
+             "    rocprofv3 --pmc WRITE_SIZE -d <dir_w> -o w --output-format csv -- python3 bench.py --pmc-probe",
+             "    python3 bench.py --pmc-summarize <dir_f>/f_counter_collection.csv <dir_w>/w_counter_collection.csv",
+             "",
+             "The probe first runs a calibration copy that reads and writes %d bytes" % CALIB_BYTES,
+             "(torch.mul(src, 1.0, out=dst) on fp32); each counter is scaled by",
+             "bytes / (counter KiB x 1024) of that copy.  The prefill figures are the second",
+             "of two prefill calls (every dispatch of the gdn kernels after its plan kernel).", "",
+             "| counter | calibration copy (KiB) | scale |", "|---|---|---|"]
+    for c, (kib, f, _) in out.items():
+        lines.append("| %s | %.0f | %.4f |" % (c, kib, f))
+    lines += ["", "| kernel | fetch (bytes) | write (bytes) |", "|---|---|---|"]
+    names = sorted(set(out["FETCH_SIZE"][2]) | set(out["WRITE_SIZE"][2]))
+    for n in names:
+        lines.append("| %s | %.0f | %.0f |" % (n, out["FETCH_SIZE"][2].get(n, 0), out["WRITE_SIZE"][2].get(n, 0)))
+    lines += ["", "traffic_bytes: %.0f" % total, "source_sha256: %s" % prefill_source_hash(), ""]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", TRAFFIC_FILE, "traffic_bytes", int(total))
+
+
+def measured_traffic():
+    """HBM bytes per prefill from the committed counter summary, or None when
+    the summary is missing or the prefill kernels changed since it was taken."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes:", "source_sha256:")))
+    if kv.get("source_sha256") != prefill_source_hash():
+        return None
+    return float(kv["traffic_bytes"])
 
 
 def main():
     args = parse()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the layer's multi-GPU "
                                    "sharding is a design note, not a measured path", "n_gpus": args.gpus}))
@@ -64,6 +183,9 @@ def main():
     import gated_deltanet_delta_amd as gdn
     import gdn_inputs as gi
 
+    if args.pmc_probe:
+        pmc_probe()
+        return
     gdn.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -206,7 +328,7 @@ def main():
                    "state_dtype": "f32", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "gdn_prefill_chunked (plan + chunk + state kernels)",
                      "achieved": round(prefill_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic()},
         "prefill": {"ms": round(ms_prefill, 4), "tokens_per_s": round(T_PREFILL / (ms_prefill * 1e-3), 1),
                     "tflops": round(prefill_tflops, 2),
                     "hbm_gbs_algorithmic": round(PREFILL_BYTES_PER_TOKEN * T_PREFILL / (ms_prefill * 1e-3) / 1e9, 1),
