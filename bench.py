@@ -12,7 +12,8 @@ finds its state in the 256 MB last-level cache left by an earlier call.
 Output: one JSON line.  `value` is prefill tokens per second over whole steps
 (T tokens per step, decode and verify included in the step time).  Extra keys
 give per-path figures measured with HIP events on the launch stream: prefill
-alone, decode state GB/s, verify GB/s, and the roofline fraction of each.
+alone (inside the steps), and decode, verify and rollback each in a loop of
+back-to-back calls over cold pools, with their GB/s and roofline fractions.
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
 """
 from __future__ import annotations
@@ -293,10 +294,34 @@ def main():
         return float(np.mean([r[a].elapsed_time(r[b]) for r in rec]))
 
     ms_prefill = avg_ms(0, 1)
-    ms_decode = avg_ms(1, 2)
-    ms_verify = avg_ms(2, 3)
-    ms_rollback = avg_ms(3, 4)
     ms_step = gpu_ms / args.steps
+
+    # Per-path times of the short calls, each in a loop of its own: inside a
+    # step, the interval after the prefill also holds the prefill's hand-back
+    # from its second stream.  Every call still finds a cold slot pool.
+    # One event pair around n back-to-back calls: the per-call time of a
+    # serving loop, inter-kernel gaps included.  (Events around each call
+    # would add their own dispatch latency, several µs at these sizes.)
+    def loop_ms(fn, n):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n_loop = 2 * len(pools)
+    ms_decode = loop_ms(lambda i: gdn.decode_step(geom, pools[i % len(pools)], dx, da, db, cw, dslot, do,
+                                                  dev_err=err), n_loop)
+    ms_verify = loop_ms(lambda i: gdn.verify_k(geom, pools[i % len(pools)], vx, va, vb, cw, vslot, snap, vo,
+                                               dev_err=err), n_loop)
+    ms_rollback = loop_ms(lambda i: gdn.rollback(geom, pools[i % len(pools)], snap, vslot, vacc, dev_err=err),
+                          n_loop)
+    if int(err.item()) != 0:
+        print(json.dumps({"error": f"device error code {int(err.item())} in the per-path loops"}))
+        sys.exit(3)
     if min(ms_prefill, ms_decode, ms_verify, ms_step) <= 0:
         print(json.dumps({"error": "a timing came out as zero"}))
         sys.exit(5)

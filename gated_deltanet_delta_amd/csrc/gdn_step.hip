@@ -23,14 +23,17 @@
 
 namespace gdn {
 
-template <int D>
+template <int D, bool VERIFY>
 struct StepShape {
   static constexpr int LPR = D / 4;              // lanes per state row (one f32x4 each)
   static constexpr int RPW = kWave / LPR;        // rows one wave covers per pass
   static constexpr int NP = D >= 64 ? 4 : (D >= 32 ? 2 : 1);  // passes per wave
   static constexpr int ROWS_WAVE = RPW * NP;
   static constexpr int NW_MAX = D / ROWS_WAVE;
-  static constexpr int NW = NW_MAX < 4 ? NW_MAX : 4;          // waves per workgroup
+  // waves per workgroup.  Decode: 8 (64 rows), which halves the workgroups
+  // that add a share of the slot's position with one contended atomic;
+  // verify (no position update, k drafts per workgroup): 4.
+  static constexpr int NW = NW_MAX < (VERIFY ? 4 : 8) ? NW_MAX : (VERIFY ? 4 : 8);
   static constexpr int ROWS_WG = NW * ROWS_WAVE;
   static constexpr int WG_PER_HEAD = D / ROWS_WG;
   static constexpr int THREADS = NW * kWave;
@@ -103,8 +106,8 @@ __device__ __forceinline__ float dot4v(f32x4_t a, float4 b) {
 // with the state (no wait on the position before the ring loads) and the
 // window rows are picked in registers.
 template <int D, bool BF16, bool VERIFY, int W, bool RING8>
-__global__ __launch_bounds__(StepShape<D>::THREADS) void step_kernel(StepArgs A) {
-  using Sh = StepShape<D>;
+__global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(StepArgs A) {
+  using Sh = StepShape<D, VERIFY>;
   constexpr int LPR = Sh::LPR;
   constexpr int NP = Sh::NP;
   constexpr int NG = D < kWave ? D : kWave;            // lanes per partial sum of squares
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(256) void rollback_kernel(StepArgs A) {
 // ---------------------------------------------------------------------------
 template <int D, bool BF16, bool VERIFY>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
-  using Sh = StepShape<D>;
+  using Sh = StepShape<D, VERIFY>;
   dim3 grid(a.Hv * Sh::WG_PER_HEAD, a.batch);
   if (a.W == 4 && a.R == 8) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, true>), grid, dim3(Sh::THREADS), 0, s, a);
   else if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, false>), grid, dim3(Sh::THREADS), 0, s, a);
