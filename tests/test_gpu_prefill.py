@@ -164,6 +164,29 @@ def test_prefill_segmented_launches():
     _check(g, inp, pool, o, heads=[0, 13, 47])
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_prefill_bf16_more_v_heads_per_k_head(G):
+    """More than three v-heads per k-head: the inverses and the -W / U'
+    products run in groups of three heads, from K K^T kept in LDS."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=G, n_slots=2)
+    inp = gi.prefill_inputs(seed=520 + G, geom=g, lengths=[150, 77], init_state=True, a_mean=-2.0)
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o)
+
+
+@pytest.mark.parametrize("n_v_heads,lengths", [(64, [70]), (64, [70, 20]), (32, [70, 20])])
+def test_prefill_single_launch_limit(n_v_heads, lengths):
+    """Chain grids of exactly 128 workgroups (one launch beside the chunk
+    kernel) and of 256 (16-chunk segments): 2 column groups per v-head."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=16, n_v_heads=n_v_heads, n_slots=len(lengths))
+    inp = gi.prefill_inputs(seed=530 + n_v_heads + len(lengths), geom=g, lengths=lengths, init_state=True,
+                            a_mean=-2.0)
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o, heads=[0, 5, n_v_heads - 1])
+
+
 def test_prefill_then_decode_continues_the_sequence():
     """Prefill the first part of a sequence, decode the rest token by token:
     matches the oracle over the whole sequence."""
