@@ -108,6 +108,13 @@ __device__ __forceinline__ float sigmoid_fast(float y) {
 __device__ __forceinline__ float silu_fast(float y) {
   return y * sigmoid_fast(y);
 }
+// SiLU of y given s = -log2(e) y (a conv whose weights carry the factor):
+// y / (1 + e^-y) = s / (-(1 + 2^s) / ln 2), one multiply fewer than silu_fast.
+constexpr float kNegLog2e = -1.4426950408889634f;
+__device__ __forceinline__ float silu_of_scaled(float s) {
+  constexpr float kNegInvLn2 = -1.4426950408889634f;  // -1 / ln 2
+  return s * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(s), kNegInvLn2, kNegInvLn2));
+}
 
 // ---------------------------------------------------------------------------
 // Device error word: the first code of a call wins.

@@ -56,7 +56,7 @@ struct PrefillArgs {
 //   head: per (chunk, v-head) block of packed -W, decayed K^T, P, U', the gate factors and V (head_bytes each)
 //   ready: per (chunk, k-head) flag, set once the chunk kernel has published that block
 struct PrefillLayout {
-  size_t kq, head, chunk_tab, seq_tab, counters, ready, total;
+  size_t kq, head, chunk_tab, seq_tab, ready, total;
   size_t kq_bytes, head_bytes;
 };
 PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int max_chunks, int n_seqs);

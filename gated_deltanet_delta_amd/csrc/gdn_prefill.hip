@@ -107,9 +107,8 @@ static PrefillLayout layout_t(int Hk, int Hv, int maxc, int S) {
   L.head_bytes = Gm::HEAD_BYTES;
   L.kq = take(mc * Hk * Gm::KQ_BYTES);
   L.head = take(mc * Hv * Gm::HEAD_BYTES);
-  L.chunk_tab = take(mc * 4 * 4);
+  L.chunk_tab = take(mc * 8 * 4);
   L.seq_tab = take(static_cast<size_t>(S) * 8 * 4);
-  L.counters = take(256);
   L.ready = take(mc * Hk * 4);
   L.total = off;
   return L;
@@ -127,6 +126,9 @@ PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int maxc, int S) 
 // Sequence table entry (int32 x 8).
 enum { SQ_FIRST = 0, SQ_NCHUNK, SQ_POS0, SQ_FLAGS, SQ_SLOT, SQ_START, SQ_LEN, SQ_PAD };
 enum { SQF_VALID = 1, SQF_INIT = 2 };
+// Chunk table entry (int32 x 8, one per chunk up to the bound): everything a
+// chunk workgroup needs in one 32-byte read.  CT_LEN is 0 past the last chunk.
+enum { CT_T0 = 0, CT_LEN, CT_SEQ_START, CT_SLOT, CT_FLAGS, CT_POS0, CT_PAD0, CT_PAD1 };
 
 template <typename T>
 __device__ __forceinline__ T* ws_ptr(void* ws, size_t off) {
@@ -140,7 +142,6 @@ __device__ __forceinline__ T* ws_ptr(void* ws, size_t off) {
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout L) {
   int32_t* ctab = ws_ptr<int32_t>(A.workspace, L.chunk_tab);
   int32_t* stab = ws_ptr<int32_t>(A.workspace, L.seq_tab);
-  int32_t* cnt = ws_ptr<int32_t>(A.workspace, L.counters);
   __shared__ int s_total;
   if (threadIdx.x == 0) {
     const int S = A.n_seqs;
@@ -172,7 +173,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
       total = 0;
     }
     if (total > A.max_chunks) total = 0;  // cannot happen for a valid partition
-    cnt[0] = total;
     s_total = total;
   }
   // every (chunk, k-head) starts unpublished
@@ -180,19 +180,27 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
   for (int i = threadIdx.x; i < A.max_chunks * A.Hk; i += blockDim.x) ready[i] = 0;
   __syncthreads();
   const int total = s_total;
-  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+  for (int c = threadIdx.x; c < A.max_chunks; c += blockDim.x) {
+    int32_t* e = ctab + 8 * c;
+    if (c >= total) {
+      for (int k = 0; k < 8; ++k) e[k] = 0;  // no chunk: CT_LEN 0
+      continue;
+    }
     int lo = 0, hi = A.n_seqs - 1;  // last s with first <= c holds c
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (stab[8 * mid + SQ_FIRST] <= c) lo = mid; else hi = mid - 1;
     }
-    const int s = lo;
-    const int i = c - stab[8 * s + SQ_FIRST];
-    const int len = stab[8 * s + SQ_LEN];
-    ctab[4 * c + 0] = s;
-    ctab[4 * c + 1] = stab[8 * s + SQ_START] + i * kC;
-    ctab[4 * c + 2] = min(kC, len - i * kC);
-    ctab[4 * c + 3] = 0;
+    const int32_t* q = stab + 8 * lo;
+    const int i = c - q[SQ_FIRST];
+    e[CT_T0] = q[SQ_START] + i * kC;
+    e[CT_LEN] = min(kC, q[SQ_LEN] - i * kC);
+    e[CT_SEQ_START] = q[SQ_START];
+    e[CT_SLOT] = q[SQ_SLOT];
+    e[CT_FLAGS] = q[SQ_FLAGS];
+    e[CT_POS0] = q[SQ_POS0];
+    e[CT_PAD0] = 0;
+    e[CT_PAD1] = 0;
   }
 }
 
@@ -421,15 +429,14 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   // order in which the chain kernel consumes them
   const int chunk = A.seg_lo + blockIdx.y;
   const int kh = blockIdx.x;
-  const int n_chunks = ws_ptr<int32_t>(A.workspace, Lay.counters)[0];
-  if (chunk >= n_chunks) return;
-  const int32_t* ce = ws_ptr<int32_t>(A.workspace, Lay.chunk_tab) + 4 * chunk;
-  const int s = ce[0], t0 = ce[1], len = ce[2];
-  const int32_t* se = ws_ptr<int32_t>(A.workspace, Lay.seq_tab) + 8 * s;
-  const bool init = (se[SQ_FLAGS] & SQF_INIT) != 0;
-  const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
-  const int slot = se[SQ_SLOT];
-  const int seq_start = se[SQ_START];
+  // one read of the chunk's table entry (no chain of dependent reads)
+  const int32_t* ce = ws_ptr<int32_t>(A.workspace, Lay.chunk_tab) + 8 * chunk;
+  const int t0 = ce[CT_T0], len = ce[CT_LEN];
+  if (len <= 0) return;
+  const bool init = (ce[CT_FLAGS] & SQF_INIT) != 0;
+  const uint32_t pos0 = static_cast<uint32_t>(ce[CT_POS0]);
+  const int slot = ce[CT_SLOT];
+  const int seq_start = ce[CT_SEQ_START];
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, C = A.C, R = A.R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const E* x = static_cast<const E*>(A.x);
@@ -490,12 +497,15 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
           raw[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
         }
       }
+      // conv weights times -log2(e): the conv then yields -log2(e) y, the
+      // argument the SiLU's exp2 takes
       float w[VE][4];
       if constexpr (KW == 4) {
 #pragma unroll
         for (int v = 0; v < VE; ++v) {
           const float4 w4 = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
-          w[v][0] = w4.x; w[v][1] = w4.y; w[v][2] = w4.z; w[v][3] = w4.w;
+          w[v][0] = kNegLog2e * w4.x; w[v][1] = kNegLog2e * w4.y;
+          w[v][2] = kNegLog2e * w4.z; w[v][3] = kNegLog2e * w4.w;
         }
       }
       auto elem = [&](const RawT& r, int v) -> float {
@@ -547,7 +557,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
                 acc = fmaf(w[v][1], hist[v][1], acc);
                 acc = fmaf(w[v][2], hist[v][2], acc);
                 acc = fmaf(w[v][3], xin, acc);
-                yy = silu_fast(acc);
+                yy = silu_of_scaled(acc);
                 hist[v][0] = hist[v][1]; hist[v][1] = hist[v][2]; hist[v][2] = xin;
               } else {
                 yy = xin;
