@@ -449,25 +449,33 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
   };
 
   // gate inputs of the v-head whose gates this wave computes (the last G
-  // waves, one head each), loaded before the conv so they arrive under it
+  // waves, one head each), loaded before the conv so they arrive under it;
+  // they stay raw until the gates are computed, so nothing waits for them here
   static_assert(kMaxGroup <= kChunkWaves, "one gate head per wave");
   const int ghi = kChunkWaves - 1 - wave;
-  float a_in = 0.f, b_in = 0.f;
+  E a_raw{}, b_raw{};
   if (ghi < G && lane < len) {
     const size_t i = static_cast<size_t>(t0 + lane) * Hv + kh * G + ghi;
-    a_in = load_in<BF16>(A.a, i);
-    b_in = load_in<BF16>(A.b, i);
+    a_raw = static_cast<const E*>(A.a)[i];
+    b_raw = static_cast<const E*>(A.b)[i];
   }
 
   // ---- conv + SiLU: item = (VE channels, 16 tokens), the 19-row window in registers.
-  // q|k items first, then v items; each wave takes a contiguous run of items. ----
+  // q|k items first, then v items; each wave takes a contiguous run of items
+  // of one kind. ----
   {
     const int nvq = 2 * D / VE, nvv = G * D / VE;
-    const int n_items = 4 * (nvq + nvv);
-    const int ipw = (n_items + kChunkWaves - 1) / kChunkWaves;
-    for (int jj = lane; jj < ipw; jj += 64) {
-      const int item = wave * ipw + jj;
-      if (item >= n_items) break;
+    const int n_qk = 4 * nvq, n_items = 4 * (nvq + nvv);
+    // q|k items on the first wq waves, v items on the rest, in proportion, so
+    // that no wave holds both kinds (a wave would run both code paths)
+    const int wq = max(1, min(kChunkWaves - 1, (2 * kChunkWaves * n_qk + n_items) / (2 * n_items)));
+    const bool qk_wave = wave < wq;
+    const int ipw = qk_wave ? (n_qk + wq - 1) / wq : (n_items - n_qk + kChunkWaves - wq - 1) / (kChunkWaves - wq);
+    const int item0 = qk_wave ? wave * ipw : n_qk + (wave - wq) * ipw;
+    const int item_end = qk_wave ? n_qk : n_items;
+    auto conv_item = [&](int jj) __attribute__((always_inline)) {
+      const int item = item0 + jj;
+      if (item >= item_end) return;
       int q, vec;
       if (item < 4 * nvq) {
         q = item / nvq;
@@ -574,30 +582,51 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
                 *reinterpret_cast<float4*>(dst + v) = make_float4(y[v][i], y[v + 1][i], y[v + 2][i], y[v + 3][i]);
             }
           } else {
-            // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16, elements i
+            // accumulator layout: tile (dv/16, quarter q), lane g4*16 + dv%16,
+            // elements i.  The VE channels of an item sit side by side in one
+            // row of a tile (dv0 is a multiple of VE), so bf16 goes out as two
+            // 16-byte stores and four lanes fill a 128-byte line.
+            E* dst = vcb + ((dv0 >> 4) * 4 + q) * 256 + (g4 * 16 + (dv0 & 15)) * 4;
+            static_assert(VE == 4, "four channels per item");
+            if constexpr (BF16) {
 #pragma unroll
-            for (int v = 0; v < VE; ++v) {
-              const int dv = dv0 + v;
-              E* dst = vcb + ((dv >> 4) * 4 + q) * 256 + (g4 * 16 + (dv & 15)) * 4;
-              if constexpr (BF16) {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(y[v][0], y[v][1]), pack2_bf16(y[v][2], y[v][3]));
-              } else {
-                *reinterpret_cast<float4*>(dst) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
-              }
+              for (int v = 0; v < VE; v += 2)
+                *reinterpret_cast<uint4*>(dst + 4 * v) =
+                    make_uint4(pack2_bf16(y[v][0], y[v][1]), pack2_bf16(y[v][2], y[v][3]),
+                               pack2_bf16(y[v + 1][0], y[v + 1][1]), pack2_bf16(y[v + 1][2], y[v + 1][3]));
+            } else {
+#pragma unroll
+              for (int v = 0; v < VE; ++v)
+                *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(y[v][0], y[v][1], y[v][2], y[v][3]);
             }
           }
         }
       };
       if (tq + 16 <= len) run(std::true_type{});
       else run(std::false_type{});
-    }
+    };
+    // the first item outside the loop: its loads go out right behind the
+    // gate inputs, with no wait between
+    if (lane < ipw) conv_item(lane);
+    for (int jj = lane + 64; jj < ipw; jj += 64) conv_item(jj);
   }
 
   // ---- gates: one wave per v-head (the last waves), lane = token, fixed-order inclusive scan ----
   if (ghi < G) {
     const int hi = ghi, h = kh * G + hi;
     float g = 0.f, bb = 0.f;
+    // the opaque copy keeps the compiler from converting (and so waiting
+    // for) the raw inputs before the conv
+    asm volatile("" : "+v"(a_raw), "+v"(b_raw));
     if (lane < len) {
+      float a_in, b_in;
+      if constexpr (BF16) {
+        a_in = bf16_bits_to_f32(a_raw);
+        b_in = bf16_bits_to_f32(b_raw);
+      } else {
+        a_in = a_raw;
+        b_in = b_raw;
+      }
       g = -softplus_f(a_in);
       bb = sigmoid_f(b_in);
     }
