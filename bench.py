@@ -12,8 +12,11 @@ finds its state in the 256 MB last-level cache left by an earlier call.
 Output: one JSON line.  `value` is prefill tokens per second over whole steps
 (T tokens per step, decode and verify included in the step time).  Extra keys
 give per-path figures measured with HIP events on the launch stream: prefill
-alone (inside the steps), and decode, verify and rollback each in a loop of
-back-to-back calls over cold pools, with their GB/s and roofline fractions.
+alone (inside the steps), and decode, verify and rollback each as the device
+time per call of a captured HIP graph of back-to-back calls over cold pools
+(the time of the same calls dispatched one by one from Python, which is bound
+by the host at these sizes, is reported beside it), with their GB/s and
+roofline fractions.
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
 """
 from __future__ import annotations
@@ -312,13 +315,41 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    # The same n calls captured once in a HIP graph and replayed: the device
+    # time per call with no host dispatch in between, as a serving loop that
+    # replays its captured token step sees it.  (Graph replays of these calls
+    # are checked against eager runs in the GPU tests.)
+    def graph_ms(fn, n, reps=4):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (n * reps)
+
     n_loop = 2 * len(pools)
-    ms_decode = loop_ms(lambda i: gdn.decode_step(geom, pools[i % len(pools)], dx, da, db, cw, dslot, do,
-                                                  dev_err=err), n_loop)
-    ms_verify = loop_ms(lambda i: gdn.verify_k(geom, pools[i % len(pools)], vx, va, vb, cw, vslot, snap, vo,
-                                               dev_err=err), n_loop)
-    ms_rollback = loop_ms(lambda i: gdn.rollback(geom, pools[i % len(pools)], snap, vslot, vacc, dev_err=err),
-                          n_loop)
+    f_decode = lambda i: gdn.decode_step(geom, pools[i % len(pools)], dx, da, db, cw, dslot, do, dev_err=err)
+    f_verify = lambda i: gdn.verify_k(geom, pools[i % len(pools)], vx, va, vb, cw, vslot, snap, vo, dev_err=err)
+    f_rollback = lambda i: gdn.rollback(geom, pools[i % len(pools)], snap, vslot, vacc, dev_err=err)
+    ms_decode_eager = loop_ms(f_decode, n_loop)
+    ms_verify_eager = loop_ms(f_verify, n_loop)
+    ms_rollback_eager = loop_ms(f_rollback, n_loop)
+    ms_decode = graph_ms(f_decode, n_loop)
+    ms_verify = graph_ms(f_verify, n_loop)
+    ms_rollback = graph_ms(f_rollback, n_loop)
     if int(err.item()) != 0:
         print(json.dumps({"error": f"device error code {int(err.item())} in the per-path loops"}))
         sys.exit(3)
@@ -360,10 +391,13 @@ def main():
                     "decode_replay_rel_err_64": consistency},
         "decode": {"us": round(ms_decode * 1e3, 2), "state_gbs": round(decode_state_gbs, 1),
                    "total_gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
+                   "timing": "graph replay", "eager_loop_us": round(ms_decode_eager * 1e3, 2),
                    "cold_pools": len(pools)},
         "verify": {"us": round(ms_verify * 1e3, 2), "gbs": round(verify_gbs, 1),
-                   "frac_hbm_peak": round(verify_gbs / HBM_PEAK_GBS, 4)},
-        "rollback": {"us": round(ms_rollback * 1e3, 2), "gbs": round(rollback_gbs, 1), "slots_copied": n_acc},
+                   "frac_hbm_peak": round(verify_gbs / HBM_PEAK_GBS, 4),
+                   "timing": "graph replay", "eager_loop_us": round(ms_verify_eager * 1e3, 2)},
+        "rollback": {"us": round(ms_rollback * 1e3, 2), "gbs": round(rollback_gbs, 1), "slots_copied": n_acc,
+                     "timing": "graph replay", "eager_loop_us": round(ms_rollback_eager * 1e3, 2)},
         "wall_s": round(wall, 3),
     }
 
