@@ -17,6 +17,8 @@ time per call of a captured HIP graph of back-to-back calls over cold pools
 (the time of the same calls dispatched one by one from Python, which is bound
 by the host at these sizes, is reported beside it), with their GB/s and
 roofline fractions.
+`prefill_varlen` times one call of the variable-length batched prefill (4
+sequences with the seeded lengths of that workload, about 101 K tokens).
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
 """
 from __future__ import annotations
@@ -50,6 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--pools", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-varlen", action="store_true", help="skip the variable-length prefill figure")
     p.add_argument("--cpu-tokens", type=int, default=1024,
                    help="prefix of the prefill sequence the CPU oracle runs on")
     p.add_argument("--pmc-probe", action="store_true",
@@ -353,6 +356,32 @@ def main():
     if int(err.item()) != 0:
         print(json.dumps({"error": f"device error code {int(err.item())} in the per-path loops"}))
         sys.exit(3)
+
+    # Variable-length batched prefill: 4 sequences with the seeded lengths of
+    # the varlen workload (about 101 K tokens), one call, event-timed.
+    varlen = None
+    if not args.no_varlen:
+        vl = gi.workload(4)
+        n_vl = int(vl["cu_seqlens"][-1])
+        s_vl = len(vl["cu_seqlens"]) - 1
+        lx = torch.from_numpy(vl["x"]).to(bf).to(dev)
+        la = torch.from_numpy(vl["a"]).to(bf).to(dev)
+        lb = torch.from_numpy(vl["b"]).to(bf).to(dev)
+        lcu = torch.from_numpy(vl["cu_seqlens"]).to(dev)
+        lslot = torch.from_numpy(vl["slots"]).to(dev)
+        lhas = torch.from_numpy(vl["has_init"]).to(dev)
+        lpool = gdn.SlotPool.zeros(geom)
+        lo = torch.empty(n_vl, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+        lws = gdn.alloc_prefill_workspace(geom, n_vl, s_vl)
+        f_vl = lambda i: gdn.prefill_chunked(geom, lpool, lx, la, lb, cw, lcu, lslot, lhas, lo, lws, dev_err=err)
+        f_vl(0)
+        ms_vl = loop_ms(f_vl, 3)
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the varlen prefill"}))
+            sys.exit(3)
+        varlen = {"n_seqs": s_vl, "tokens": n_vl, "lengths": [int(v) for v in np.diff(vl["cu_seqlens"])],
+                  "us": round(ms_vl * 1e3, 1), "tokens_per_s": round(n_vl / (ms_vl * 1e-3), 1)}
+        del lx, la, lb, lo, lws, lpool
     if min(ms_prefill, ms_decode, ms_verify, ms_step) <= 0:
         print(json.dumps({"error": "a timing came out as zero"}))
         sys.exit(5)
@@ -398,6 +427,7 @@ def main():
                    "timing": "graph replay", "eager_loop_us": round(ms_verify_eager * 1e3, 2)},
         "rollback": {"us": round(ms_rollback * 1e3, 2), "gbs": round(rollback_gbs, 1), "slots_copied": n_acc,
                      "timing": "graph replay", "eager_loop_us": round(ms_rollback_eager * 1e3, 2)},
+        "prefill_varlen": varlen,
         "wall_s": round(wall, 3),
     }
 

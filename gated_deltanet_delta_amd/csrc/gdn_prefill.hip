@@ -961,6 +961,35 @@ __device__ __forceinline__ int chain_logical_index(int L, int nwg) {
   return (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
 }
 
+// One sequence as a chain launch sees it: the sequence's chunks in [c0,
+// c0 + ncl) of the chunk table are this launch's; the state carries over
+// between launches through the slot (fp32, exact).  A sequence without chunks
+// belongs to the launch that starts at chunk 0.  False: nothing to do here.
+struct ChainSeq {
+  bool init, seq_last, state_in;
+  int slot, seq_start, len, c0, cr0, ncl;
+  uint32_t pos0;
+};
+__device__ __forceinline__ bool chain_seq(const PrefillArgs& A, const PrefillLayout& Lay, int s, ChainSeq& q) {
+  const int32_t* se = ws_ptr<int32_t>(A.workspace, Lay.seq_tab) + 8 * s;
+  if (!(se[SQ_FLAGS] & SQF_VALID)) return false;
+  const int first = se[SQ_FIRST], nc = se[SQ_NCHUNK];
+  const int c0 = max(first, A.seg_lo), c1 = min(first + nc, A.seg_hi);
+  if (nc == 0 ? A.seg_lo != 0 : c0 >= c1) return false;
+  const bool seq_first = nc == 0 || c0 == first;  // the sequence starts in this launch
+  q.init = (se[SQ_FLAGS] & SQF_INIT) != 0;
+  q.seq_last = nc == 0 || c1 == first + nc;       // ... and ends in it
+  q.state_in = seq_first ? q.init : true;
+  q.slot = se[SQ_SLOT];
+  q.seq_start = se[SQ_START];
+  q.len = se[SQ_LEN];
+  q.c0 = c0;
+  q.cr0 = c0 - first;
+  q.ncl = c1 - c0;
+  q.pos0 = static_cast<uint32_t>(se[SQ_POS0]);
+  return true;
+}
+
 // Chain workgroup: CW compute waves (wave w holds rows 16 (z CW + w) ..) and
 // kLoaders loader waves.  While the compute waves work on chunk c from one
 // LDS buffer, the loaders copy chunk c+1 (the Q tiles of the k-head, the -W /
@@ -981,288 +1010,308 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
   __shared__ __attribute__((aligned(1024))) char lds1[Sm::BUF];
 
   const int q = chain_logical_index(blockIdx.x, gridDim.x);
-  const int zb = q % Z, h = (q / Z) % A.Hv, s = q / (Z * A.Hv);
+  const int zb = q % Z, h = (q / Z) % A.Hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
   const int dvt = zb * CW + wave;                // a compute wave's 16 rows of d_v
-  const int32_t* se = ws_ptr<int32_t>(A.workspace, Lay.seq_tab) + 8 * s;
-  if (!(se[SQ_FLAGS] & SQF_VALID)) return;
-  const bool init = (se[SQ_FLAGS] & SQF_INIT) != 0;
-  const int first = se[SQ_FIRST], nc = se[SQ_NCHUNK], slot = se[SQ_SLOT];
-  const int seq_start = se[SQ_START], len = se[SQ_LEN];
-  const uint32_t pos0 = static_cast<uint32_t>(se[SQ_POS0]);
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk, kh = h / G;
   const int g = lane >> 4, col = lane & 15;
-  // This launch covers the sequence's chunks in [c0, c1) of the chunk table;
-  // the state carries over between launches through the slot (fp32, exact).
-  // A sequence without chunks belongs to the launch that starts at chunk 0.
-  const int c0 = max(first, A.seg_lo), c1 = min(first + nc, A.seg_hi);
-  if (nc == 0 ? A.seg_lo != 0 : c0 >= c1) return;
-  const bool seq_first = nc == 0 || c0 == first;     // the sequence starts in this launch
-  const bool seq_last = nc == 0 || c1 == first + nc;  // ... and ends in it
-  const bool state_in = seq_first ? init : true;
-  const int cr0 = c0 - first, ncl = c1 - c0;          // first chunk (within the sequence) and count
-  float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
+  // A persistent launch has one workgroup per (v-head, row block) that walks
+  // the sequences in table order, the order in which the chunk kernel
+  // publishes their chunks; a segment launch has one workgroup per sequence
+  // as well.  Loader and compute waves walk the same sequences and take the
+  // same barriers for each; at the end of a sequence the loaders write the
+  // q|k channels of its conv history and the compute waves the v channels.
+  const int s_lo = A.persistent ? 0 : q / (Z * A.Hv);
+  const int s_hi = A.persistent ? A.n_seqs : s_lo + 1;
 
   // ---- loader waves: two chunks in flight in registers ----
   if (wave >= CW) {
-    constexpr int NL = Sm::NL;
-    const int lw = wave - CW;
-    const char* wsb = static_cast<const char*>(A.workspace);
-    // 1 KB blocks [Q | -W, K^T, P | U' | gates]; loader lw copies blocks
-    // NL j + lw.  Every segment starts at a multiple of NL blocks, so the
-    // segment of round j is known at compile time.
-    constexpr int NKQ = Sm::NKQ, NHT = Sm::NHT, NVW = Sm::NVW, NBLK = NKQ + NHT + NVW + 1;
-    constexpr int NJ = (NBLK + NL - 1) / NL;
-    static_assert(NKQ % NL == 0 && NHT % NL == 0 && NVW % NL == 0 && Sm::VW % 1024 == 0, "segment alignment");
-    static_assert(Sm::GATES <= 1024, "gates fit one block");
-    static_assert(NBLK * 1024 == static_cast<int>(Sm::BUF), "blocks fill the buffer");
-    // Both register sets are always filled (a chunk past the end reloads the
-    // last chunk into unused registers), so their accesses stay unconditional.
-    const int clast = c0 + (ncl > 0 ? ncl - 1 : 0);
-    // In a persistent launch the chunk kernel runs concurrently: wait until it
-    // has published (chunk, kh).  The flag is read with an agent-scope atomic
-    // (it bypasses this XCD's L2); the operand lines read after it were not
-    // touched earlier by this kernel, so they come from memory.  The wait is
-    // bounded: on time-out the error word is set and the loader goes on.
-    const int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
-    bool timed_out = false;
-    auto wait_ready = [&](int chunk) {
-      if (!A.persistent || timed_out) return;
-      const int32_t* f = ready + chunk * Hk + kh;
-      for (int spins = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kReadySpins) {
-          report_error(A.dev_err, GDN_DEV_WAIT_TIMEOUT);
-          timed_out = true;
-          break;
+    for (int s = s_lo; s < s_hi; ++s) {
+      ChainSeq sq;
+      if (!chain_seq(A, Lay, s, sq)) continue;
+      const bool init = sq.init, seq_last = sq.seq_last;
+      const int slot = sq.slot, seq_start = sq.seq_start, len = sq.len, c0 = sq.c0, ncl = sq.ncl;
+      const uint32_t pos0 = sq.pos0;
+      constexpr int NL = Sm::NL;
+      const int lw = wave - CW;
+      const char* wsb = static_cast<const char*>(A.workspace);
+      // 1 KB blocks [Q | -W, K^T, P | U' | gates]; loader lw copies blocks
+      // NL j + lw.  Every segment starts at a multiple of NL blocks, so the
+      // segment of round j is known at compile time.
+      constexpr int NKQ = Sm::NKQ, NHT = Sm::NHT, NVW = Sm::NVW, NBLK = NKQ + NHT + NVW + 1;
+      constexpr int NJ = (NBLK + NL - 1) / NL;
+      static_assert(NKQ % NL == 0 && NHT % NL == 0 && NVW % NL == 0 && Sm::VW % 1024 == 0, "segment alignment");
+      static_assert(Sm::GATES <= 1024, "gates fit one block");
+      static_assert(NBLK * 1024 == static_cast<int>(Sm::BUF), "blocks fill the buffer");
+      // Both register sets are always filled (a chunk past the end reloads the
+      // last chunk into unused registers), so their accesses stay unconditional.
+      const int clast = c0 + (ncl > 0 ? ncl - 1 : 0);
+      // In a persistent launch the chunk kernel runs concurrently: wait until it
+      // has published (chunk, kh).  The flag is read with an agent-scope atomic
+      // (it bypasses this XCD's L2); the operand lines read after it were not
+      // touched earlier by this kernel, so they come from memory.  The wait is
+      // bounded: on time-out the error word is set and the loader goes on.
+      const int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
+      bool timed_out = false;
+      auto wait_ready = [&](int chunk) {
+        if (!A.persistent || timed_out) return;
+        const int32_t* f = ready + chunk * Hk + kh;
+        for (int spins = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kReadySpins) {
+            report_error(A.dev_err, GDN_DEV_WAIT_TIMEOUT);
+            timed_out = true;
+            break;
+          }
+        }
+      };
+      auto fetch = [&](uint4 (&r)[NJ], int chunk) {
+        chunk = min(chunk, clast);
+        wait_ready(chunk);
+        const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
+        const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
+        const char* vwb = hb + Gm::VW_OFF + static_cast<size_t>(zb) * CW * 4 * P::VC_BYTES;
+        // an opaque copy of this lane's offset keeps the compiler from hoisting
+        // one address register per block out of the chunk loop
+        int lo = lw * 1024 + lane * 16;
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int b0 = j * NL;                     // first block of this round
+          const char* src;
+          if (b0 < NKQ) src = kq + b0 * 1024;
+          else if (b0 < NKQ + NHT) src = hb + (b0 - NKQ) * 1024;
+          else if (b0 < NKQ + NHT + NVW) src = vwb + (b0 - NKQ - NHT) * 1024;
+          else src = hb + Gm::GATE_OFF - lw * 1024;  // gates: loader 0, lanes < GATES / 16
+          r[j] = (b0 + NL <= NKQ + NHT + NVW || (lw == 0 && lane * 16 < static_cast<int>(Sm::GATES)))
+                     ? *reinterpret_cast<const uint4*>(src + lo)
+                     : make_uint4(0, 0, 0, 0);
+        }
+      };
+      auto put = [&](const uint4 (&r)[NJ], char* base) {
+        int lo = lw * 1024 + lane * 16;
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (j + 1 < NJ || lw == 0) *reinterpret_cast<uint4*>(base + j * NL * 1024 + lo) = r[j];
+      };
+      // Before barrier i the buffer (i % 2) holds chunk c0 + i; chunk i+1 and
+      // i+2 are in flight in the two register sets meanwhile.
+      uint4 ra[NJ], rb[NJ];
+      if (ncl > 0) {  // a sequence without chunks stages nothing (its chunk index may be past the table)
+        fetch(ra, c0);
+        fetch(rb, c0 + 1);
+        put(ra, lds0);
+      }
+      lds_barrier();
+      if (ncl > 0) fetch(ra, c0 + 2);
+      for (int ci = 0; ci < ncl; ci += 2) {
+        put(rb, lds1);            // chunk ci + 1 (past the end: never read)
+        lds_barrier();
+        fetch(rb, c0 + ci + 3);
+        if (ci + 1 < ncl) {
+          put(ra, lds0);          // chunk ci + 2
+          lds_barrier();
+          fetch(ra, c0 + ci + 4);
         }
       }
-    };
-    auto fetch = [&](uint4 (&r)[NJ], int chunk) {
-      chunk = min(chunk, clast);
-      wait_ready(chunk);
-      const char* kq = wsb + Lay.kq + (static_cast<size_t>(chunk) * Hk + kh) * Gm::KQ_BYTES;
-      const char* hb = wsb + Lay.head + (static_cast<size_t>(chunk) * Hv + h) * Gm::HEAD_BYTES;
-      const char* vwb = hb + Gm::VW_OFF + static_cast<size_t>(zb) * CW * 4 * P::VC_BYTES;
-      // an opaque copy of this lane's offset keeps the compiler from hoisting
-      // one address register per block out of the chunk loop
-      int lo = lw * 1024 + lane * 16;
-      asm volatile("" : "+v"(lo));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int b0 = j * NL;                     // first block of this round
-        const char* src;
-        if (b0 < NKQ) src = kq + b0 * 1024;
-        else if (b0 < NKQ + NHT) src = hb + (b0 - NKQ) * 1024;
-        else if (b0 < NKQ + NHT + NVW) src = vwb + (b0 - NKQ - NHT) * 1024;
-        else src = hb + Gm::GATE_OFF - lw * 1024;  // gates: loader 0, lanes < GATES / 16
-        r[j] = (b0 + NL <= NKQ + NHT + NVW || (lw == 0 && lane * 16 < static_cast<int>(Sm::GATES)))
-                   ? *reinterpret_cast<const uint4*>(src + lo)
-                   : make_uint4(0, 0, 0, 0);
+      // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
+      if (A.W > 0 && seq_last) {
+        const int W = A.W, C = A.C, R = A.R;
+        const uint32_t pos_end = (init ? pos0 : 0u) + static_cast<uint32_t>(len);
+        float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
+        auto put = [&](int c) {
+          for (int i = 1; i < W; ++i) {
+            const int rel = len - i;
+            float* dst = ring + static_cast<size_t>(ring_row(pos_end - i, R)) * C + c;
+            if (rel >= 0) *dst = load_in<BF16>(A.x, static_cast<size_t>(seq_start + rel) * C + c);
+            else if (!init) *dst = 0.f;
+          }
+        };
+        if (h % G == 0 && zb == 0)
+          for (int cc = tid - CW * 64; cc < 2 * D; cc += Sm::NL * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
       }
-    };
-    auto put = [&](const uint4 (&r)[NJ], char* base) {
-      int lo = lw * 1024 + lane * 16;
-      asm volatile("" : "+v"(lo));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (j + 1 < NJ || lw == 0) *reinterpret_cast<uint4*>(base + j * NL * 1024 + lo) = r[j];
-    };
-    // Before barrier i the buffer (i % 2) holds chunk c0 + i; chunk i+1 and
-    // i+2 are in flight in the two register sets meanwhile.
-    uint4 ra[NJ], rb[NJ];
-    if (ncl > 0) {  // a sequence without chunks stages nothing (its chunk index may be past the table)
-      fetch(ra, c0);
-      fetch(rb, c0 + 1);
-      put(ra, lds0);
-    }
-    lds_barrier();
-    if (ncl > 0) fetch(ra, c0 + 2);
-    for (int ci = 0; ci < ncl; ci += 2) {
-      put(rb, lds1);            // chunk ci + 1 (past the end: never read)
-      lds_barrier();
-      fetch(rb, c0 + ci + 3);
-      if (ci + 1 < ncl) {
-        put(ra, lds0);          // chunk ci + 2
-        lds_barrier();
-        fetch(ra, c0 + ci + 4);
-      }
-    }
+    }  // sequences
   } else {
+    for (int s = s_lo; s < s_hi; ++s) {
+      ChainSeq sq;
+      if (!chain_seq(A, Lay, s, sq)) continue;
+      const bool init = sq.init, seq_last = sq.seq_last, state_in = sq.state_in;
+      const int slot = sq.slot, seq_start = sq.seq_start, len = sq.len, cr0 = sq.cr0, ncl = sq.ncl;
+      const uint32_t pos0 = sq.pos0;
+      float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
 
-  // ---- compute waves: S^T slice in accumulators, tile i holds S^T[16i + 4g + e][16 dvt + col] ----
-  f32x4_t st[NT];
+      // ---- compute waves: S^T slice in accumulators, tile i holds S^T[16i + 4g + e][16 dvt + col] ----
+      f32x4_t st[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    if (state_in) {
-      const float4 v = *reinterpret_cast<const float4*>(Sglob + 16 * i + 4 * g);
-      st[i] = f32x4_t{v.x, v.y, v.z, v.w};
-    } else {
-      st[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+      for (int i = 0; i < NT; ++i) {
+        if (state_in) {
+          const float4 v = *reinterpret_cast<const float4*>(Sglob + 16 * i + 4 * g);
+          st[i] = f32x4_t{v.x, v.y, v.z, v.w};
+        } else {
+          st[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
 
-  // One chunk step from an LDS buffer; O returned in registers.  The body
-  // runs in stages separated by scheduling barriers: every stage issues the
-  // LDS reads of the operand tiles the NEXT stage multiplies, so those reads
-  // are in flight while this stage's MFMAs run (a wave has no other wave on
-  // its SIMD to hide LDS latency behind).
-  auto compute = [&](const char* base, f32x4_t (&O)[4]) {
-    const uint4* qa = reinterpret_cast<const uint4*>(base);
-    const uint4* ht = reinterpret_cast<const uint4*>(base + Sm::KQ);
-    const E* vw = reinterpret_cast<const E*>(base + Sm::KQ + Sm::HT) + wave * 4 * 256;
-    const float* gt = reinterpret_cast<const float*>(base + Sm::KQ + Sm::HT + Sm::VW);
-    auto tile = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
-    auto fence = [] {
+      // One chunk step from an LDS buffer; O returned in registers.  The body
+      // runs in stages separated by scheduling barriers: every stage issues the
+      // LDS reads of the operand tiles the NEXT stage multiplies, so those reads
+      // are in flight while this stage's MFMAs run (a wave has no other wave on
+      // its SIMD to hide LDS latency behind).
+      auto compute = [&](const char* base, f32x4_t (&O)[4]) {
+        const uint4* qa = reinterpret_cast<const uint4*>(base);
+        const uint4* ht = reinterpret_cast<const uint4*>(base + Sm::KQ);
+        const E* vw = reinterpret_cast<const E*>(base + Sm::KQ + Sm::HT) + wave * 4 * 256;
+        const float* gt = reinterpret_cast<const float*>(base + Sm::KQ + Sm::HT + Sm::VW);
+        auto tile = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
+        auto fence = [] {
 #if GDN_CHAIN_SCHED
-      __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);
 #endif
-    };
+        };
 
-    // stage 0: -W tiles, U', e^{G_last}
-    uint4 wa[4][KSD];
+        // stage 0: -W tiles, U', e^{G_last}
+        uint4 wa[4][KSD];
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
+        for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) wa[mt][ks] = tile(ht + Gm::WA * 64, mt * KSD + ks);
-    f32x4_t U[4];
+          for (int mt = 0; mt < 4; ++mt) wa[mt][ks] = tile(ht + Gm::WA * 64, mt * KSD + ks);
+        f32x4_t U[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if constexpr (BF16) {
-        const uint2 r2 = *reinterpret_cast<const uint2*>(vw + mt * 256 + lane * 4);
-        U[mt] = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                        __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
-      } else {
-        const float4 r4 = *reinterpret_cast<const float4*>(vw + mt * 256 + lane * 4);
-        U[mt] = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+        for (int mt = 0; mt < 4; ++mt) {
+          if constexpr (BF16) {
+            const uint2 r2 = *reinterpret_cast<const uint2*>(vw + mt * 256 + lane * 4);
+            U[mt] = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                            __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
+          } else {
+            const float4 r4 = *reinterpret_cast<const float4*>(vw + mt * 256 + lane * 4);
+            U[mt] = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+          }
+        }
+        const float eGl = gt[kC];
+        // B operands of S^T (d_k in packed order)
+        Bop bS[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int i0 = ks * TPS;
+          bS[ks] = Ch::bop(st[i0], (TPS == 2 && i0 + 1 < NT) ? st[(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
+        fence();
+        // stage 1: U = U' - W S^T; read the Q tiles
+        uint4 qt[4][KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) qt[mt][ks] = tile(qa, mt * KSD + ks);
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) U[mt] = Ch::step(wa[mt][ks], bS[ks], U[mt]);
+        fence();
+        // stage 2: Y = Q S^T, S^T scaled by e^{G_last}; read the decayed K^T tiles
+        uint4 kd[NT][KSC];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+          for (int i = 0; i < NT; ++i) kd[i][ks] = tile(ht + Gm::KDA * 64, i * KSC + ks);
+        f32x4_t Y[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) Y[mt] = Ch::step(qt[mt][ks], bS[ks], Y[mt]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) st[i] = st[i] * eGl;
+        Bop bU[KSC];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) bU[ks] = Ch::bop(U[ks * TPS], U[(ks * TPS + 1) % 4]);
+        fence();
+        // stage 3: S^T <- e^{G_last} S^T + (diag(e^{G_last - G}) K)^T U; read the P tiles and e^G
+        uint4 pt[4][KSC];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks * P::SK < 16 * (mt + 1)) pt[mt][ks] = tile(ht + Gm::PA * 64, mt * KSC + ks);
+        float4 eg[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) eg[mt] = *reinterpret_cast<const float4*>(gt + 16 * mt + 4 * g);
+#pragma unroll
+        for (int ip = 0; ip < NT; ip += 2)
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+            for (int i = ip; i < ip + 2 && i < NT; ++i) st[i] = Ch::step(kd[i][ks], bU[ks], st[i]);
+        fence();
+        // stage 4: O = diag(e^G) Y + P U
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4_t o = Y[mt] * f32x4_t{eg[mt].x, eg[mt].y, eg[mt].z, eg[mt].w};
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks * P::SK < 16 * (mt + 1)) o = Ch::step(pt[mt][ks], bU[ks], o);
+          O[mt] = o;
+        }
+      };
+
+      // O of chunk ci (tokens seq_start + 64 ci + 16 mt + 4 g + i, column 16 dvt + col)
+      const size_t rowstride = static_cast<size_t>(Hv) * D;
+      auto store_o = [&](int ci, const f32x4_t (&O)[4]) {
+        const int clen = min(kC, len - kC * ci);
+        E* ob = static_cast<E*>(A.o) + (static_cast<size_t>(seq_start + kC * ci + 4 * g)) * rowstride + h * D + 16 * dvt + col;
+        if (clen == kC) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * mt + 4 * g + i < clen) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
+        }
+      };
+
+      {
+        f32x4_t O[4];
+        lds_barrier();  // the first chunk staged
+        for (int ci = 0; ci < ncl; ci += 2) {
+          if (ci > 0) store_o(cr0 + ci - 1, O);
+          compute(lds0, O);
+          lds_barrier();
+          if (ci + 1 < ncl) {
+            store_o(cr0 + ci, O);
+            compute(lds1, O);
+            lds_barrier();
+          }
+        }
+        if (ncl > 0) store_o(cr0 + ncl - 1, O);
       }
-    }
-    const float eGl = gt[kC];
-    // B operands of S^T (d_k in packed order)
-    Bop bS[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const int i0 = ks * TPS;
-      bS[ks] = Ch::bop(st[i0], (TPS == 2 && i0 + 1 < NT) ? st[(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
-    }
-    fence();
-    // stage 1: U = U' - W S^T; read the Q tiles
-    uint4 qt[4][KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) qt[mt][ks] = tile(qa, mt * KSD + ks);
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) U[mt] = Ch::step(wa[mt][ks], bS[ks], U[mt]);
-    fence();
-    // stage 2: Y = Q S^T, S^T scaled by e^{G_last}; read the decayed K^T tiles
-    uint4 kd[NT][KSC];
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-      for (int i = 0; i < NT; ++i) kd[i][ks] = tile(ht + Gm::KDA * 64, i * KSC + ks);
-    f32x4_t Y[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) Y[mt] = Ch::step(qt[mt][ks], bS[ks], Y[mt]);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) st[i] = st[i] * eGl;
-    Bop bU[KSC];
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) bU[ks] = Ch::bop(U[ks * TPS], U[(ks * TPS + 1) % 4]);
-    fence();
-    // stage 3: S^T <- e^{G_last} S^T + (diag(e^{G_last - G}) K)^T U; read the P tiles and e^G
-    uint4 pt[4][KSC];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks)
-        if (ks * P::SK < 16 * (mt + 1)) pt[mt][ks] = tile(ht + Gm::PA * 64, mt * KSC + ks);
-    float4 eg[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) eg[mt] = *reinterpret_cast<const float4*>(gt + 16 * mt + 4 * g);
-#pragma unroll
-    for (int ip = 0; ip < NT; ip += 2)
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-        for (int i = ip; i < ip + 2 && i < NT; ++i) st[i] = Ch::step(kd[i][ks], bU[ks], st[i]);
-    fence();
-    // stage 4: O = diag(e^G) Y + P U
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4_t o = Y[mt] * f32x4_t{eg[mt].x, eg[mt].y, eg[mt].z, eg[mt].w};
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks)
-        if (ks * P::SK < 16 * (mt + 1)) o = Ch::step(pt[mt][ks], bU[ks], o);
-      O[mt] = o;
-    }
-  };
 
-  // O of chunk ci (tokens seq_start + 64 ci + 16 mt + 4 g + i, column 16 dvt + col)
-  const size_t rowstride = static_cast<size_t>(Hv) * D;
-  auto store_o = [&](int ci, const f32x4_t (&O)[4]) {
-    const int clen = min(kC, len - kC * ci);
-    E* ob = static_cast<E*>(A.o) + (static_cast<size_t>(seq_start + kC * ci + 4 * g)) * rowstride + h * D + 16 * dvt + col;
-    if (clen == kC) {
+      // ---- final state back to the slot ----
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * mt + 4 * g + i < clen) ob[(16 * mt + i) * rowstride] = to_e<BF16>(O[mt][i]);
-    }
-  };
-
-  {
-    f32x4_t O[4];
-    lds_barrier();  // the first chunk staged
-    for (int ci = 0; ci < ncl; ci += 2) {
-      if (ci > 0) store_o(cr0 + ci - 1, O);
-      compute(lds0, O);
-      lds_barrier();
-      if (ci + 1 < ncl) {
-        store_o(cr0 + ci, O);
-        compute(lds1, O);
-        lds_barrier();
+      for (int i = 0; i < NT; ++i)
+        *reinterpret_cast<float4*>(Sglob + 16 * i + 4 * g) = make_float4(st[i][0], st[i][1], st[i][2], st[i][3]);
+      // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
+      if (A.W > 0 && seq_last) {
+        const int W = A.W, C = A.C, R = A.R;
+        const uint32_t pos_end = (init ? pos0 : 0u) + static_cast<uint32_t>(len);
+        float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
+        auto put = [&](int c) {
+          for (int i = 1; i < W; ++i) {
+            const int rel = len - i;
+            float* dst = ring + static_cast<size_t>(ring_row(pos_end - i, R)) * C + c;
+            if (rel >= 0) *dst = load_in<BF16>(A.x, static_cast<size_t>(seq_start + rel) * C + c);
+            else if (!init) *dst = 0.f;
+          }
+        };
+        if (lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
+        if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
       }
-    }
-    if (ncl > 0) store_o(cr0 + ncl - 1, O);
-  }
-
-  // ---- final state back to the slot ----
-#pragma unroll
-  for (int i = 0; i < NT; ++i)
-    *reinterpret_cast<float4*>(Sglob + 16 * i + 4 * g) = make_float4(st[i][0], st[i][1], st[i][2], st[i][3]);
-  }  // compute waves
-
-  // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
-  if (A.W > 0 && seq_last) {
-    const int W = A.W, C = A.C, R = A.R;
-    const uint32_t pos_end = (init ? pos0 : 0u) + static_cast<uint32_t>(len);
-    float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
-    auto put = [&](int c) {
-      for (int i = 1; i < W; ++i) {
-        const int rel = len - i;
-        float* dst = ring + static_cast<size_t>(ring_row(pos_end - i, R)) * C + c;
-        if (rel >= 0) *dst = load_in<BF16>(A.x, static_cast<size_t>(seq_start + rel) * C + c);
-        else if (!init) *dst = 0.f;
-      }
-    };
-    if (h % G == 0 && zb == 0)
-      for (int cc = tid; cc < 2 * D; cc += (CW + Sm::NL) * 64) put(cc < D ? kh * D + cc : Hk * D + kh * D + (cc - D));
-    if (wave < CW && lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
-    if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
+    }  // sequences
   }
 }
 
@@ -1331,12 +1380,14 @@ static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
   e = static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
   if (e) return e;
-  const int chain_wgs = a0.n_seqs * a0.Hv * (Geo<D, BF16>::NT / CW);
+  const int chain_wgs_seq = a0.Hv * (Geo<D, BF16>::NT / CW);  // chain workgroups per sequence
   const dim3 chain_block((CW + ChainSmem<D, BF16, CW>::NL) * 64);
-  if (chain_wgs <= kPersistentChainMax && a0.max_chunks <= 65535) {  // 65535: grid y limit
-    // One chain launch over whole sequences, beside one chunk launch over all
-    // chunks: the chain's loaders wait on each (chunk, k-head) flag.  The chain
-    // grid holds at most half the CUs, so chunk workgroups always find CUs.
+  if (chain_wgs_seq <= kPersistentChainMax && a0.max_chunks <= 65535) {  // 65535: grid y limit
+    // One chain launch over all sequences in turn, beside one chunk launch
+    // over all chunks: the chain's loaders wait on each (chunk, k-head) flag.
+    // The chain grid holds at most half the CUs, so chunk workgroups always
+    // find CUs.
+    const int chain_wgs = chain_wgs_seq;
     PrefillArgs a = a0;
     a.persistent = 1;
     a.seg_lo = 0;
@@ -1354,6 +1405,7 @@ static int launch_prefill_fit(const PrefillArgs& a0, hipStream_t st) {
       if (e) return e;
     }
   } else {
+    const int chain_wgs = a0.n_seqs * chain_wgs_seq;
     // at least one segment, so that sequences without tokens still get their slot written
     int seg = 0;
     for (int lo = 0; lo == 0 || lo < a0.max_chunks; lo += kSegChunks, ++seg) {

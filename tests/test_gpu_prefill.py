@@ -155,10 +155,22 @@ def test_prefill_reused_workspace_sees_new_inputs():
 
 
 def test_prefill_segmented_launches():
-    """A chain grid above the single-launch limit (2 sequences x 48 v-heads x
-    2 column groups) runs as 16-chunk launch segments."""
-    g = dataclasses.replace(gi.GEOM_QWEN, n_slots=2)
+    """A chain grid above the single-launch limit for one sequence (96 v-heads
+    x 2 column groups) runs as 16-chunk launch segments."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=16, n_v_heads=96, n_slots=2)
     inp = gi.prefill_inputs(seed=503, geom=g, lengths=[1100, 70], init_state=True, a_mean=-2.0)
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    _check(g, inp, pool, o, heads=[0, 13, 95])
+
+
+@pytest.mark.parametrize("lengths", [[300, 0, 130, 64], [64, 1, 129]])
+def test_prefill_one_launch_walks_the_sequences(lengths):
+    """Several sequences in one chain launch: every chain workgroup takes the
+    sequences in turn (an empty one in between, a one-token one), each from
+    its own slot's initial state."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_slots=len(lengths) + 1)
+    inp = gi.prefill_inputs(seed=540 + len(lengths), geom=g, lengths=lengths, init_state=True, a_mean=-2.0)
     pool, o, err = _prefill(g, inp)
     assert err == 0
     _check(g, inp, pool, o, heads=[0, 13, 47])
@@ -175,10 +187,11 @@ def test_prefill_bf16_more_v_heads_per_k_head(G):
     _check(g, inp, pool, o)
 
 
-@pytest.mark.parametrize("n_v_heads,lengths", [(64, [70]), (64, [70, 20]), (32, [70, 20])])
+@pytest.mark.parametrize("n_v_heads,lengths", [(64, [70]), (64, [70, 20]), (32, [70, 20]), (80, [70, 20])])
 def test_prefill_single_launch_limit(n_v_heads, lengths):
-    """Chain grids of exactly 128 workgroups (one launch beside the chunk
-    kernel) and of 256 (16-chunk segments): 2 column groups per v-head."""
+    """Chain grids of exactly 128 workgroups per sequence (one launch beside
+    the chunk kernel, for one or two sequences) and of 160 (16-chunk
+    segments): 2 column groups per v-head."""
     g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=16, n_v_heads=n_v_heads, n_slots=len(lengths))
     inp = gi.prefill_inputs(seed=530 + n_v_heads + len(lengths), geom=g, lengths=lengths, init_state=True,
                             a_mean=-2.0)
