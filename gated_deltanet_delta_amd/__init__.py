@@ -23,6 +23,7 @@ GDN_F32 = 0
 GDN_BF16 = 1
 GDN_FLAG_L2NORM_QK = 1
 POS_ONE = 65536
+POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
 DEV_OK = 0
@@ -172,7 +173,7 @@ class SlotPool:
 
     state: torch.Tensor       # fp32 [n_slots][H_v][d_v][d_k]
     conv_state: torch.Tensor  # fp32 [n_slots][R][C]
-    conv_pos: torch.Tensor    # int32 [n_slots], units of 1/65536 token
+    conv_pos: torch.Tensor    # int32 [n_slots][POS_STRIDE], position in column 0, units of 1/65536 token
 
     @staticmethod
     def zeros(geom: Geometry, device="cuda") -> "SlotPool":
@@ -180,14 +181,14 @@ class SlotPool:
         return SlotPool(
             torch.zeros(geom.n_slots, geom.n_v_heads, geom.d_v, geom.d_k, dtype=torch.float32, device=device),
             torch.zeros(geom.n_slots, R, C, dtype=torch.float32, device=device),
-            torch.zeros(geom.n_slots, dtype=torch.int32, device=device))
+            torch.zeros(geom.n_slots, POS_STRIDE, dtype=torch.int32, device=device))
 
 
 def _check_pool(geom: Geometry, pool: SlotPool):
     _need(pool.state, "state", (geom.n_slots, geom.n_v_heads, geom.d_v, geom.d_k), torch.float32)
     if geom.conv_width > 0:
         _need(pool.conv_state, "conv_state", (geom.n_slots, geom.conv_ring, geom.conv_channels), torch.float32)
-        _need(pool.conv_pos, "conv_pos", (geom.n_slots,), torch.int32)
+        _need(pool.conv_pos, "conv_pos", (geom.n_slots, POS_STRIDE), torch.int32)
 
 
 # --------------------------------------------------------------------------

@@ -4,10 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
 
 constexpr int kWave = 64;
 constexpr int kPosShift = 16;  // conv_pos counts tokens in units of 1/65536
+constexpr int kPosStride = GDN_POS_STRIDE;  // a slot's position is conv_pos[slot * kPosStride]
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
       int32_t* e = stab + 8 * s;
       e[SQ_FIRST] = total;
       e[SQ_NCHUNK] = nc;
-      e[SQ_POS0] = (init && A.W > 0 && ok) ? static_cast<int32_t>(static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0;
+      e[SQ_POS0] = (init && A.W > 0 && ok) ? static_cast<int32_t>(static_cast<uint32_t>(A.conv_pos[slot * kPosStride]) >> kPosShift) : 0;
       e[SQ_FLAGS] = SQF_VALID | (init ? SQF_INIT : 0);
       e[SQ_SLOT] = slot;
       e[SQ_START] = st;
@@ -1309,7 +1309,7 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
           }
         };
         if (lane < 16) put(2 * Hk * D + h * D + 16 * dvt + lane);
-        if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot] = static_cast<int32_t>(pos_end << kPosShift);
+        if (h == 0 && zb == 0 && tid == 0) A.conv_pos[slot * kPosStride] = static_cast<int32_t>(pos_end << kPosShift);
       }
     }  // sequences
   }

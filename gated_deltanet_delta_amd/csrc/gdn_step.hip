@@ -156,7 +156,7 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
 
   // ---- the ring position, then the state rows (the position is requested
   // first: loads complete in order, so the ring rows below wait for it alone) ----
-  const uint32_t pos = W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift) : 0u;
+  const uint32_t pos = W > 0 ? (static_cast<uint32_t>(A.conv_pos[slot * kPosStride]) >> kPosShift) : 0u;
   __builtin_amdgcn_sched_barrier(0);
   const float* Sg = A.state + (static_cast<size_t>(slot) * A.Hv + h) * D * D;
   f32x4_t S[NP];
@@ -248,7 +248,7 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
       const uint32_t nwg = gridDim.x;
       const uint32_t one = 1u << kPosShift;
       const uint32_t share = one / nwg + (blockIdx.x < one % nwg ? 1u : 0u);
-      atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot), share);
+      atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot * kPosStride), share);
     }
     // ---- L2 norm of q and k, gates ----
     float sqq = 0.f, skk = 0.f;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void conv_step_kernel(StepArgs A) {
   }
   const int C = A.C, R = A.R;
   const float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
-  const uint32_t pos = static_cast<uint32_t>(A.conv_pos[slot]) >> kPosShift;
+  const uint32_t pos = static_cast<uint32_t>(A.conv_pos[slot * kPosStride]) >> kPosShift;
   const void* xb = static_cast<const char*>(A.x) + static_cast<size_t>(b) * C * (BF16 ? 2 : 4);
   if (c < C) {
     const float y = conv1<BF16, W>(ring, pos, R, xb, C, A.conv_w, 0, c);
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void conv_step_kernel(StepArgs A) {
     const uint32_t nwg = gridDim.x;
     const uint32_t one = 1u << kPosShift;
     const uint32_t share = one / nwg + (blockIdx.x < one % nwg ? 1u : 0u);
-    atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot), share);
+    atomicAdd(reinterpret_cast<unsigned int*>(A.conv_pos + slot * kPosStride), share);
   }
 }
 
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void rollback_kernel(StepArgs A) {
     if (e < nvec) store_nt4(dst + e * 4, load4(src + e * 4));
   }
   if (A.W > 0 && h == 0 && blockIdx.x == 0 && threadIdx.x == 0)
-    A.conv_pos[slot] = static_cast<int32_t>(static_cast<uint32_t>(A.conv_pos[slot]) +
+    A.conv_pos[slot * kPosStride] = static_cast<int32_t>(static_cast<uint32_t>(A.conv_pos[slot * kPosStride]) +
                                             (static_cast<uint32_t>(n) << kPosShift));
 }
 

@@ -50,8 +50,11 @@
  * ---------------------------------------
  *  state      fp32  [n_slots][H_v][d_v][d_k]   slot pool of recurrent states
  *  conv_state fp32  [n_slots][R][C]            conv ring of past inputs x
- *  conv_pos   int32 [n_slots]                  ring position, in units of
- *                                              1/GDN_POS_ONE token (below)
+ *  conv_pos   int32 [n_slots][GDN_POS_STRIDE]  ring position of slot s in
+ *                                              conv_pos[s][0], in units of
+ *                                              1/GDN_POS_ONE token (below);
+ *                                              words 1.. of a row are never
+ *                                              read or written
  *  conv_w     fp32  [C][W]                     tap W-1 multiplies the current token
  *  x          dtype_in  [rows][C]              projected input, q | k | v
  *  a, b       dtype_in  [rows][H_v]            raw gate inputs
@@ -65,7 +68,9 @@
  * p = (uint32_t)conv_pos >> 16.  The ring must hold R >= W-1+max_draft rows
  * (R a power of two) so verify can write its drafts ahead of the committed
  * history without overwriting it.  Zero-initialising a slot's ring and
- * conv_pos gives an all-zero history.
+ * conv_pos gives an all-zero history.  Each slot's position has a 128-byte
+ * line of its own (GDN_POS_STRIDE words), so that the position updates of
+ * different slots in one call do not contend for one line of the cache.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -77,8 +82,9 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_POS_ONE 65536
+#define GDN_POS_STRIDE 32 /* int32 words per slot in conv_pos */
 
 typedef enum gdn_status {
   GDN_OK = 0,

@@ -62,7 +62,7 @@ def make_pool(g: gi.Geometry, state, hist, pos):
             for i in range(W - 1):  # hist row i is token pos-(W-1)+i
                 ring[s, (int(pos[s]) - (W - 1) + i) % R] = hist[s, i]
         pool.conv_state.copy_(torch.from_numpy(ring))
-        pool.conv_pos.copy_(torch.from_numpy((np.asarray(pos, np.int64) * gi_pos_one()).astype(np.int32)))
+        pool.conv_pos[:, 0].copy_(torch.from_numpy((np.asarray(pos, np.int64) * gi_pos_one()).astype(np.int32)))
     return pool
 
 
@@ -73,7 +73,7 @@ def gi_pos_one() -> int:
 
 def positions(pool) -> np.ndarray:
     """Token positions of every slot (conv_pos / 65536, as unsigned)."""
-    p = pool.conv_pos.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    p = pool.conv_pos[:, 0].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
     return p >> 16
 
 

@@ -61,7 +61,8 @@ def test_decode_workload2_full():
     pos = H.positions(pool)
     for s in range(g.n_slots):
         assert pos[s] == inp["pos"][s] + (1 if s in inp["slots"] else 0)
-    assert np.all((pool.conv_pos.cpu().numpy() & 0xFFFF) == 0)
+    assert np.all((pool.conv_pos[:, 0].cpu().numpy() & 0xFFFF) == 0)
+    assert not pool.conv_pos[:, 1:].any()  # the rest of each slot's line is never written
 
 
 def test_decode_tight_error_bound():

@@ -132,4 +132,4 @@ def test_rollback_bad_accepted_reported():
     s0, s1, s2 = (int(s) for s in inp["slots"][:3])
     assert torch.equal(pool.state[s0], snap[0, 0])
     assert torch.equal(pool.state[s1], before[s1]) and torch.equal(pool.state[s2], before[s2])
-    assert pool.conv_pos[s1] == pos_before[s1] and pool.conv_pos[s2] == pos_before[s2]
+    assert torch.equal(pool.conv_pos[s1], pos_before[s1]) and torch.equal(pool.conv_pos[s2], pos_before[s2])
