@@ -15,6 +15,8 @@ Sources.  The pages this build follows are cited by title and section:
             Gated DeltaNet, arXiv:2412.06464.  Section 3 also states that the
             state has a fixed size whatever the context length; section 4.1
             prints the state byte counts; section 9 keeps states in fp32.
+            Sections 3, 4.2 and 6.1 motivate state checkpoints at block
+            boundaries for prefix reuse and measure their cost.
   [Forge]   "Forge: how I wrote my own inference engine and beat llama.cpp".
             Entry of 27 August: speculative verify of k draft rows, with
             state snapshots between rows so that rollback is a copy.
@@ -302,6 +304,54 @@ def prefill(geom, x, a, b, conv_w, cu_seqlens, S0s, hist0s, has_init, heads=None
                                             S0, h0, heads=heads)
         finals.append((S_T, h_T))
     return o, finals
+
+
+def prefill_checkpoints(geom, x, a, b, conv_w, cu_seqlens, S0s, hist0s, has_init, every,
+                        heads=None):
+    """Variable-length prefill that also keeps the state at block boundaries.
+
+    [Hybrid] section 3: a later request can reuse a shared prefix only through
+    a copy of the state saved where the prefix ends, since the live state goes
+    on to absorb the first request's own tail; section 4.2: such snapshots are
+    taken at every cache-block boundary, and section 6.1 measures what writing
+    them costs the prefill.  Here checkpoint j of sequence s is the state after
+    the first (j+1)*every tokens of s, for every (j+1)*every <= len(s): the
+    final state of the layer run over those tokens alone.  Each sequence runs
+    block by block, the state and the conv history of one block starting the
+    next.  Checkpoints are numbered sequence by sequence, in token order.
+
+    Returns (o, finals, ckpts, where): o and finals as ``prefill``; ckpts
+    (n, len(heads), d_v, d_k); where[i] = (s, p), checkpoint i taken after p
+    tokens of sequence s.
+    """
+    if every <= 0:
+        raise ValueError("every must be positive")
+    N = x.shape[0]
+    H = geom.n_v_heads
+    heads = np.arange(H) if heads is None else np.asarray(heads)
+    o = np.empty((N, len(heads), geom.d_v), F64)
+    finals, ckpts, where = [], [], []
+    for s in range(len(cu_seqlens) - 1):
+        t0, t1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        if has_init[s]:
+            S_full, hist = np.array(S0s[s], F64), np.asarray(hist0s[s], F64)
+        else:
+            S_full = np.zeros((H, geom.d_v, geom.d_k), F64)
+            hist = np.zeros((max(geom.conv_width - 1, 0), geom.conv_channels), F64)
+        S_heads = S_full[heads]
+        for p0 in range(t0, t1, every):
+            p1 = min(p0 + every, t1)
+            o[p0:p1], S_heads, hist = layer_sequence(geom, x[p0:p1], a[p0:p1], b[p0:p1],
+                                                     conv_w, S_full, hist, heads=heads)
+            S_full = np.zeros((H, geom.d_v, geom.d_k), F64)
+            S_full[heads] = S_heads
+            if p1 - p0 == every:
+                ckpts.append(np.array(S_heads))
+                where.append((s, p1 - t0))
+        finals.append((S_heads, hist))
+    ck = (np.stack(ckpts) if ckpts
+          else np.zeros((0, len(heads), geom.d_v, geom.d_k), F64))
+    return o, finals, ck, where
 
 
 # ----------------------------------------------------------------------------

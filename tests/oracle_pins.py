@@ -419,4 +419,65 @@ def pin_prefill_is_per_sequence(m):
     _close(fin[1][0], S2b, 1e-13, "seq 1 final state")
 
 
+
+def _ckpt_case(rng, geom, lens, has_init):
+    C, H = geom.conv_channels, geom.n_v_heads
+    N = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    x = rng.normal(size=(N, C))
+    a = rng.normal(-1.0, 1.0, size=(N, H))
+    b = rng.normal(size=(N, H))
+    w = rng.normal(size=(C, geom.conv_width))
+    S0 = 0.5 * rng.normal(size=(len(lens), H, geom.d_v, geom.d_k))
+    h0 = rng.normal(size=(len(lens), geom.conv_width - 1, C))
+    return cu, x, a, b, w, S0, h0
+
+
+def pin_checkpoints_beta_zero(m):
+    """beta = 0 (b far below zero): checkpoint after p tokens = e^{sum_{t<p} g_t} S_0,
+    which fixes both the positions and the count of the checkpoints."""
+    geom = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=2, d_k=4, d_v=4)
+    rng = _rng(33)
+    lens, every = [13, 0, 8, 4], 4
+    cu, x, a, b, w, S0, h0 = _ckpt_case(rng, geom, lens, [1, 0, 1, 0])
+    b[:] = -1000.0
+    o, fin, ck, where = m.prefill_checkpoints(geom, x, a, b, w, cu, S0, h0, [1, 0, 1, 0], every)
+    want = [(s, p) for s, n in enumerate(lens) for p in range(every, n + 1, every)]
+    assert where == want, (where, want)
+    assert ck.shape == (len(want), 2, 4, 4)
+    g = -np.logaddexp(0.0, a)
+    for i, (s, p) in enumerate(want):
+        start = S0[s] if s in (0, 2) else np.zeros_like(S0[s])
+        ref = np.exp(g[cu[s]:cu[s] + p].sum(axis=0))[:, None, None] * start
+        _close(ck[i], ref, 1e-13, f"beta=0 checkpoint {i} (seq {s}, p {p})")
+
+
+def pin_checkpoints_chunked_prefix(m):
+    """Checkpoint after p tokens equals the chunked form (an independent
+    derivation) run over the first p tokens with the front end applied; a
+    sequence whose length is a multiple of the block ends on a checkpoint equal
+    to its final state; outputs equal the plain prefill's."""
+    geom = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=3, d_k=4, d_v=4)
+    rng = _rng(34)
+    lens, every, init = [14, 10, 5], 5, [1, 0, 1]
+    cu, x, a, b, w, S0, h0 = _ckpt_case(rng, geom, lens, init)
+    heads = [2, 0]
+    o, fin, ck, where = m.prefill_checkpoints(geom, x, a, b, w, cu, S0, h0, init, every,
+                                              heads=heads)
+    assert [p for _, p in where] == [5, 10, 5, 10, 5]
+    oref, finref = m.prefill(geom, x, a, b, w, cu, S0, h0, init, heads=heads)
+    _close(o, oref, 1e-13, "outputs vs plain prefill")
+    g, _, beta = m.gates(a, b)
+    for i, (s, p) in enumerate(where):
+        t0 = cu[s]
+        start = S0[s] if init[s] else np.zeros_like(S0[s])
+        hist = h0[s] if init[s] else np.zeros_like(h0[s])
+        q, k, v = m.frontend_sequence(geom, x[t0:t0 + p], w, hist)
+        _, Sc = m.chunked_recurrence(q[:, heads], k[:, heads], v[:, heads], g[t0:t0 + p][:, heads],
+                                     beta[t0:t0 + p][:, heads], start[heads], 3, geom.q_scale)
+        _close(ck[i], Sc, 1e-11, f"checkpoint {i} (seq {s}, p {p}) vs chunked prefix")
+        if p == lens[s]:
+            _close(ck[i], fin[s][0], 1e-15, f"seq {s} ends on its last checkpoint")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

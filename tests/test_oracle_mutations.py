@@ -42,6 +42,12 @@ MUTATIONS = [
     ("rollback_off_by_one", "return np.array(snaps[accepted - 1]), np.array(hists[accepted - 1])",
      "return np.array(snaps[accepted - 1 if accepted < len(snaps) else accepted - 2]), "
      "np.array(hists[accepted - 1])"),
+    ("checkpoint_partial_block", "            if p1 - p0 == every:\n",
+     "            if p1 - p0 >= 1:\n"),
+    ("checkpoint_history_reset", "conv_w, S_full, hist, heads=heads)",
+     "conv_w, S_full, 0 * hist, heads=heads)"),
+    ("checkpoint_position_relative_to_batch", "where.append((s, p1 - t0))",
+     "where.append((s, p1))"),
     ("state_bytes_fp16", "return 4 * n_slots * geom.n_v_heads", "return 2 * n_slots * geom.n_v_heads"),
 ]
 
