@@ -19,6 +19,8 @@ by the host at these sizes, is reported beside it), with their GB/s and
 roofline fractions.
 `prefill_varlen` times one call of the variable-length batched prefill (4
 sequences with the seeded lengths of that workload, about 101 K tokens).
+`prefill_ckpt` times the T = 8192 prefill that also writes the state every 512
+tokens, beside the same prefill without checkpoints.
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
 """
 from __future__ import annotations
@@ -43,6 +45,7 @@ DECODE_BYTES = 26_116_864                      # cfg: 4 slots x 1 token
 DECODE_STATE_BYTES = 25_165_824                # state read + write
 VERIFY_BYTES = 64_752_640                      # 4 slots x k = 4, snapshots written
 ROLLBACK_BYTES_PER_SLOT = 6_291_456
+CKPT_EVERY = 512                               # tokens between state checkpoints
 
 
 def parse():
@@ -53,6 +56,7 @@ def parse():
     p.add_argument("--pools", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-varlen", action="store_true", help="skip the variable-length prefill figure")
+    p.add_argument("--no-ckpt", action="store_true", help="skip the checkpoint-prefill figure")
     p.add_argument("--cpu-tokens", type=int, default=1024,
                    help="prefix of the prefill sequence the CPU oracle runs on")
     p.add_argument("--pmc-probe", action="store_true",
@@ -382,6 +386,32 @@ def main():
         varlen = {"n_seqs": s_vl, "tokens": n_vl, "lengths": [int(v) for v in np.diff(vl["cu_seqlens"])],
                   "us": round(ms_vl * 1e3, 1), "tokens_per_s": round(n_vl / (ms_vl * 1e-3), 1)}
         del lx, la, lb, lo, lws, lpool
+    # The T = 8192 prefill that also writes a state checkpoint every 512 tokens
+    # (16 checkpoints of 3 MiB), against the same prefill without them, both
+    # timed the same way (event pair around back-to-back calls).
+    ckpt_fig = None
+    if not args.no_ckpt:
+        every = CKPT_EVERY
+        ck = torch.empty(T_PREFILL // every, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+        f_plain = lambda i: gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err)
+        f_ck = lambda i: gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err,
+                                             ckpt=ck, ckpt_every=every)
+        f_ck(0)
+        torch.cuda.synchronize()
+        # the last checkpoint of a sequence that ends on a boundary is its final state
+        if not torch.equal(ck[-1], ppool.state[int(pslot[0])]):
+            print(json.dumps({"error": "the last checkpoint differs from the final state"}))
+            sys.exit(4)
+        ms_plain = min(loop_ms(f_plain, 5) for _ in range(2))
+        ms_ck = min(loop_ms(f_ck, 5) for _ in range(2))
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the checkpoint prefill"}))
+            sys.exit(3)
+        ck_bytes = ck.numel() * 4
+        ckpt_fig = {"every": every, "n_ckpt": int(ck.shape[0]), "ckpt_bytes": ck_bytes,
+                    "us": round(ms_ck * 1e3, 1), "plain_us": round(ms_plain * 1e3, 1),
+                    "overhead_pct": round(100.0 * (ms_ck - ms_plain) / ms_plain, 2)}
+        del ck
     if min(ms_prefill, ms_decode, ms_verify, ms_step) <= 0:
         print(json.dumps({"error": "a timing came out as zero"}))
         sys.exit(5)
@@ -428,6 +458,7 @@ def main():
         "rollback": {"us": round(ms_rollback * 1e3, 2), "gbs": round(rollback_gbs, 1), "slots_copied": n_acc,
                      "timing": "graph replay", "eager_loop_us": round(ms_rollback_eager * 1e3, 2)},
         "prefill_varlen": varlen,
+        "prefill_ckpt": ckpt_fig,
         "wall_s": round(wall, 3),
     }
 

@@ -72,6 +72,9 @@ _SIGS = {
                                        _P, _P, _P]),
     "gdn_prefill_chunked": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P, _P]),
+    "gdn_prefill_chunked_ckpt": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _I, _P,
+                                                ctypes.c_size_t, _P, _P]),
     "gdn_verify_k": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
                                     _P, _P, _P, _P]),
     "gdn_rollback": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _I, _P, _P]),
@@ -272,8 +275,14 @@ def alloc_prefill_workspace(geom: Geometry, n_tokens: int, n_seqs: int, device="
 
 
 def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens, slot, has_init, o,
-                    workspace, dev_err=None, stream=None):
-    """gdn_prefill_chunked: varlen chunked prefill; final states and histories go to the slots."""
+                    workspace, dev_err=None, stream=None, ckpt=None, ckpt_every=0):
+    """gdn_prefill_chunked: varlen chunked prefill; final states and histories go to the slots.
+
+    With ckpt_every > 0 it calls gdn_prefill_chunked_ckpt instead, which also
+    writes the state after every ckpt_every tokens of each sequence into ckpt,
+    an fp32 device tensor [n][H_v][d_v][d_k] with n >= n_tokens // ckpt_every
+    (see ``checkpoint_count`` for the number a partition produces).
+    """
     N = x.shape[0]
     S = slot.shape[0]
     C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
@@ -291,14 +300,35 @@ def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens,
         raise ValueError("workspace: must be a contiguous device tensor")
     g = geom.c_struct()
     nbytes = workspace.numel() * workspace.element_size()
+    if ckpt_every:
+        cap = N // ckpt_every if ckpt_every > 0 else 0
+        if ckpt is None and cap == 0:
+            ck_bytes = 0
+        else:
+            if (ckpt is None or not ckpt.is_cuda or ckpt.dtype != torch.float32 or not ckpt.is_contiguous()
+                    or ckpt.dim() != 4 or tuple(ckpt.shape[1:]) != (Hv, dv, geom.d_k)):
+                raise ValueError(f"ckpt: need a contiguous float32 device tensor [n][{Hv}][{dv}][{geom.d_k}]")
+            ck_bytes = ckpt.numel() * 4
+        _check(lib().gdn_prefill_chunked_ckpt(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
+                                              _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w),
+                                              _ptr(cu_seqlens), _ptr(slot), _ptr(has_init), S, N, CHUNK,
+                                              _ptr(workspace), nbytes, _ptr(o), int(ckpt_every), _ptr(ckpt),
+                                              ck_bytes, _ptr(dev_err), _stream(stream)))
+        return
     _check(lib().gdn_prefill_chunked(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
                                      _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w),
                                      _ptr(cu_seqlens), _ptr(slot), _ptr(has_init), S, N, CHUNK,
                                      _ptr(workspace), nbytes, _ptr(o), _ptr(dev_err), _stream(stream)))
 
 
+def checkpoint_count(seq_lens, ckpt_every: int) -> int:
+    """Checkpoints gdn_prefill_chunked_ckpt writes for these sequence lengths."""
+    return sum(int(n) // ckpt_every for n in seq_lens)
+
+
 __all__ = [
     "Geometry", "GdnGeometry", "GdnError", "SlotPool", "lib", "conv_state_step", "decode_step", "verify_k",
-    "rollback", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace", "POS_ONE", "CHUNK",
+    "rollback", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
+    "checkpoint_count", "POS_ONE", "CHUNK",
     "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS",
 ]

@@ -145,6 +145,13 @@ gdn_status check_batch(int32_t batch, const gdn_geometry* g) {
 
 }  // namespace
 
+static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                               const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                               const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
+                               int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
+                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name);
+
 extern "C" {
 
 const char* gdn_status_string(gdn_status s) {
@@ -308,6 +315,33 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
                                const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
                                int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                size_t workspace_bytes, void* o, int32_t* dev_err, void* stream) {
+  return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
+                      n_tokens, chunk, workspace, workspace_bytes, o, 0, nullptr, 0, dev_err, stream,
+                      "gdn_prefill_chunked");
+}
+
+gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                                    const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                                    const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
+                                    int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
+                                    size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
+                                    size_t ckpt_bytes, int32_t* dev_err, void* stream) {
+  if (ckpt_every <= 0 || ckpt_every % gdn::kChunk != 0)
+    return fail(GDN_ERR_RANGE, "ckpt_every: %d, required: a positive multiple of %d", ckpt_every, gdn::kChunk);
+  return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
+                      n_tokens, chunk, workspace, workspace_bytes, o, ckpt_every, ckpt, ckpt_bytes, dev_err,
+                      stream, "gdn_prefill_chunked_ckpt");
+}
+
+}  // extern "C"
+
+// Both prefill entry points: checks, then the launch.  ckpt_every == 0: no checkpoints.
+static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                               const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                               const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
+                               int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
+                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name) {
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   if (chunk != gdn::kChunk)
@@ -364,7 +398,15 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
   a.flags = g->flags;
   a.q_scale = g->q_scale;
   a.l2_eps = g->l2_eps;
-  return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream), "gdn_prefill_chunked");
+  if (ckpt_every > 0) {
+    const size_t n_ckpt = static_cast<size_t>(n_tokens / ckpt_every);
+    const size_t per = static_cast<size_t>(g->n_v_heads) * g->d_v * g->d_k * sizeof(float);
+    if (ckpt_bytes < n_ckpt * per)
+      return fail(GDN_ERR_RANGE, "ckpt_bytes: %zu, required: >= %zu (%zu checkpoints of %zu bytes)", ckpt_bytes,
+                  n_ckpt * per, n_ckpt, per);
+    if (n_ckpt > 0) GDN_NEED_PTR(ckpt, "ckpt");
+    a.ckpt = ckpt;
+    a.ckpt_every = ckpt_every;
+  }
+  return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream), name);
 }
-
-}  // extern "C"

@@ -49,6 +49,8 @@ struct PrefillArgs {
   float q_scale, l2_eps;
   int32_t seg_lo, seg_hi;  // chunk-table range of one launch segment (set by the launcher)
   int32_t persistent;      // 1: one chain launch over whole sequences, waiting on per-chunk ready flags
+  float* ckpt;             // state checkpoints [n][Hv][D][D], or null
+  int32_t ckpt_every;      // tokens between checkpoints (a multiple of kChunk), 0: none
 };
 
 // Byte offsets and block sizes of the prefill workspace.

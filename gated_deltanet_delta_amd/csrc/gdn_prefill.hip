@@ -124,7 +124,8 @@ PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int maxc, int S) 
 }
 
 // Sequence table entry (int32 x 8).
-enum { SQ_FIRST = 0, SQ_NCHUNK, SQ_POS0, SQ_FLAGS, SQ_SLOT, SQ_START, SQ_LEN, SQ_PAD };
+// SQ_CKPT0: index of the sequence's first state checkpoint.
+enum { SQ_FIRST = 0, SQ_NCHUNK, SQ_POS0, SQ_FLAGS, SQ_SLOT, SQ_START, SQ_LEN, SQ_CKPT0 };
 enum { SQF_VALID = 1, SQF_INIT = 2 };
 // Chunk table entry (int32 x 8, one per chunk up to the bound): everything a
 // chunk workgroup needs in one 32-byte read.  CT_LEN is 0 past the last chunk.
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
     const int S = A.n_seqs;
     bool ok = A.cu_seqlens[0] == 0 && A.cu_seqlens[S] == A.n_tokens;
     int bad_code = ok ? 0 : GDN_DEV_BAD_SEQLENS;
-    int total = 0;
+    int total = 0, n_ckpt = 0;
     for (int s = 0; s < S; ++s) {
       const int st = A.cu_seqlens[s];
       const int len = A.cu_seqlens[s + 1] - st;
@@ -164,8 +165,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
       e[SQ_SLOT] = slot;
       e[SQ_START] = st;
       e[SQ_LEN] = len;
-      e[SQ_PAD] = 0;
+      e[SQ_CKPT0] = n_ckpt;
       total += nc;
+      if (A.ckpt_every > 0 && len > 0) n_ckpt += len / A.ckpt_every;
     }
     if (!ok) {
       report_error(A.dev_err, bad_code);
@@ -967,7 +969,7 @@ __device__ __forceinline__ int chain_logical_index(int L, int nwg) {
 // belongs to the launch that starts at chunk 0.  False: nothing to do here.
 struct ChainSeq {
   bool init, seq_last, state_in;
-  int slot, seq_start, len, c0, cr0, ncl;
+  int slot, seq_start, len, c0, cr0, ncl, ckpt0;
   uint32_t pos0;
 };
 __device__ __forceinline__ bool chain_seq(const PrefillArgs& A, const PrefillLayout& Lay, int s, ChainSeq& q) {
@@ -987,6 +989,7 @@ __device__ __forceinline__ bool chain_seq(const PrefillArgs& A, const PrefillLay
   q.cr0 = c0 - first;
   q.ncl = c1 - c0;
   q.pos0 = static_cast<uint32_t>(se[SQ_POS0]);
+  q.ckpt0 = se[SQ_CKPT0];
   return true;
 }
 
@@ -1139,6 +1142,7 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
       if (!chain_seq(A, Lay, s, sq)) continue;
       const bool init = sq.init, seq_last = sq.seq_last, state_in = sq.state_in;
       const int slot = sq.slot, seq_start = sq.seq_start, len = sq.len, cr0 = sq.cr0, ncl = sq.ncl;
+      const int ckpt0 = sq.ckpt0;
       const uint32_t pos0 = sq.pos0;
       float* Sglob = A.state + (static_cast<size_t>(slot) * Hv + h) * D * D + static_cast<size_t>(16 * dvt + col) * D;
 
@@ -1275,16 +1279,32 @@ __global__ __launch_bounds__((CW + ChainSmem<D, BF16, CW>::NL) * 64, 1) void cha
         }
       };
 
+      // State checkpoint after chunk ci of the sequence when its end is a
+      // multiple of ckpt_every tokens (a partial last chunk never is one); the
+      // same layout and store pattern as the final state.
+      auto store_ckpt = [&](int ci) {
+        if (A.ckpt_every <= 0) return;
+        const int done = kC * (ci + 1);
+        if (done > len || done % A.ckpt_every != 0) return;
+        float* cb = A.ckpt + (static_cast<size_t>(ckpt0 + done / A.ckpt_every - 1) * Hv + h) * D * D +
+                    static_cast<size_t>(16 * dvt + col) * D;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          *reinterpret_cast<float4*>(cb + 16 * i + 4 * g) = make_float4(st[i][0], st[i][1], st[i][2], st[i][3]);
+      };
+
       {
         f32x4_t O[4];
         lds_barrier();  // the first chunk staged
         for (int ci = 0; ci < ncl; ci += 2) {
           if (ci > 0) store_o(cr0 + ci - 1, O);
           compute(lds0, O);
+          store_ckpt(cr0 + ci);
           lds_barrier();
           if (ci + 1 < ncl) {
             store_o(cr0 + ci, O);
             compute(lds1, O);
+            store_ckpt(cr0 + ci + 1);
             lds_barrier();
           }
         }

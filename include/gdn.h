@@ -209,6 +209,40 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
                                size_t workspace_bytes, void* o, int32_t* dev_err, void* stream);
 
 /*
+ * gdn_prefill_chunked that also writes state checkpoints at block boundaries
+ * ("Hybrid transformers under load", section 3: reusing a shared prefix needs
+ * a saved copy of the state where the prefix ends, since the live state goes
+ * on to absorb the rest of the request; section 4.2: such snapshots are taken
+ * at every cache-block boundary; section 6.1 measures their cost).
+ * Everything gdn_prefill_chunked computes and writes is computed and written
+ * the same way, bit for bit; in addition, for each sequence s and each
+ * p = ckpt_every, 2 ckpt_every, ... <= n_s, the state after the first p tokens
+ * of s (counted within this call) is written to
+ *   ckpt fp32 [n_ckpt][H_v][d_v][d_k],
+ * numbered sequence by sequence in token order: sequence s's checkpoints start
+ * at index sum over s' < s of floor(n_s' / ckpt_every).  A sequence whose
+ * length is a multiple of ckpt_every ends on a checkpoint equal to its final
+ * state.  The conv history at checkpoint p is not written: with
+ * ckpt_every >= 64 > W-1 it is the input rows x[cu_seqlens[s] + p - W + 1 ..
+ * cu_seqlens[s] + p - 1], which the caller holds.  Entries past the last
+ * checkpoint are not touched.
+ *   ckpt_every: a positive multiple of `chunk` (checkpoints fall on chunk ends).
+ *   ckpt: device, 16-byte aligned, ckpt_bytes >= floor(n_tokens / ckpt_every)
+ *   * H_v * d_v * d_k * 4 (no partition of n_tokens has more checkpoints);
+ *   NULL only when that bound is 0.
+ * Errors as gdn_prefill_chunked, plus GDN_ERR_RANGE for ckpt_every and
+ * ckpt_bytes.
+ */
+gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* conv_state,
+                                    int32_t* conv_pos, const void* x, const void* a, const void* b,
+                                    const float* conv_w, const int32_t* cu_seqlens,
+                                    const int32_t* slot, const int32_t* has_init, int32_t n_seqs,
+                                    int32_t n_tokens, int32_t chunk, void* workspace,
+                                    size_t workspace_bytes, void* o, int32_t ckpt_every,
+                                    float* ckpt, size_t ckpt_bytes, int32_t* dev_err,
+                                    void* stream);
+
+/*
  * Speculative verify of k draft tokens per batch row ("Forge", 27 August:
  * the DeltaNet state walks the draft rows in order, with a snapshot of the
  * state after every row).  For draft j = 0..k-1 it computes the same per-token

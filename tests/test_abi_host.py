@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gdn_conv_state_step", "gdn_decode_step", "gdn_prefill_chunked", "gdn_verify_k", "gdn_rollback"):
+    for n in ("gdn_conv_state_step", "gdn_decode_step", "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt",
+              "gdn_verify_k", "gdn_rollback"):
         assert n in names
 
 
@@ -157,6 +158,30 @@ def test_prefill_refusals(gdn):
     g.dtype_in = g.dtype_out = gdn.GDN_F32
     assert call() == 4
     assert "d_k: 128 with dtype_in GDN_F32" in L.gdn_last_error().decode()
+
+
+def test_prefill_checkpoint_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn)
+    need = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 8192, 1)
+    per = g.n_v_heads * g.d_v * g.d_k * 4
+
+    def call(every=512, ck=_p(), ck_bytes=16 * per, n_tokens=8192):
+        return L.gdn_prefill_chunked_ckpt(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                                          _p(), 1, n_tokens, 64, _p(), need, _p(), every, ck, ck_bytes, None, None)
+    for bad in (0, -64, 100, 528):
+        assert call(every=bad) == 5
+        assert f"ckpt_every: {bad}, required: a positive multiple of 64" in L.gdn_last_error().decode()
+    assert call(ck_bytes=16 * per - 1) == 5
+    assert f"required: >= {16 * per} (16 checkpoints of {per} bytes)" in L.gdn_last_error().decode()
+    assert call(ck=None) == 1
+    assert "ckpt: NULL" in L.gdn_last_error().decode()
+    assert call(ck=ctypes.c_void_p(4096 + 8)) == 2
+    # fewer tokens than one block: no checkpoint can be due, so no buffer is needed
+    # (the call stops at the next missing pointer, the state)
+    st = L.gdn_prefill_chunked_ckpt(ctypes.byref(g), None, _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                                    1, 500, 64, _p(), need, _p(), 512, None, 0, None, None)
+    assert st == 1 and "state: NULL" in L.gdn_last_error().decode()
 
 
 def test_conv_step_refusals(gdn):
