@@ -20,7 +20,12 @@ roofline fractions.
 `prefill_varlen` times one call of the variable-length batched prefill (4
 sequences with the seeded lengths of that workload, about 101 K tokens).
 `prefill_ckpt` times the T = 8192 prefill that also writes the state every 512
-tokens, beside the same prefill without checkpoints.
+tokens, beside the same prefill without checkpoints.  `decode_batch` times the
+decode step at 16, 64 and 256 slots (graph replays over cold pools), each
+beside a plain device copy of the same state bytes.  `verify_economics` times
+verify(k) for k = 1 .. 4 and turns it, with rollback and decode, into the cost
+of a speculative round in decode steps and the acceptance rate at which the
+round pays (E[tokens] = (1 - p^(k+1)) / (1 - p)).
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill.
 """
 from __future__ import annotations
@@ -46,6 +51,35 @@ DECODE_STATE_BYTES = 25_165_824                # state read + write
 VERIFY_BYTES = 64_752_640                      # 4 slots x k = 4, snapshots written
 ROLLBACK_BYTES_PER_SLOT = 6_291_456
 CKPT_EVERY = 512                               # tokens between state checkpoints
+DECODE_SWEEP = (16, 64, 256)                   # decode batch sizes of the sweep
+
+
+def expected_tokens(p: float, k: int) -> float:
+    """Mean tokens per speculative round of k drafts, each accepted with
+    probability p until the first rejection, plus the one token the verify
+    pass produces itself: (1 - p^(k+1)) / (1 - p) ("Forge", section on the
+    formulas that decide everything)."""
+    if p >= 1.0:
+        return float(k + 1)
+    return (1.0 - p ** (k + 1)) / (1.0 - p)
+
+
+def break_even_acceptance(cost_steps: float, k: int):
+    """Acceptance p at which a round that costs `cost_steps` decode steps
+    yields as many tokens as those steps would (expected_tokens = cost_steps);
+    0 if the round is never dearer than one step, None if it never pays."""
+    if cost_steps <= 1.0:
+        return 0.0
+    if cost_steps >= k + 1:
+        return None
+    lo, hi = 0.0, 1.0
+    for _ in range(200):  # expected_tokens rises monotonically in p
+        mid = 0.5 * (lo + hi)
+        if expected_tokens(mid, k) < cost_steps:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
 
 
 def parse():
@@ -57,6 +91,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-varlen", action="store_true", help="skip the variable-length prefill figure")
     p.add_argument("--no-ckpt", action="store_true", help="skip the checkpoint-prefill figure")
+    p.add_argument("--no-decode-sweep", action="store_true", help="skip the decode batch sweep")
+    p.add_argument("--no-economics", action="store_true", help="skip the verify(k) round economics")
     p.add_argument("--cpu-tokens", type=int, default=1024,
                    help="prefix of the prefill sequence the CPU oracle runs on")
     p.add_argument("--pmc-probe", action="store_true",
@@ -412,6 +448,74 @@ def main():
                     "us": round(ms_ck * 1e3, 1), "plain_us": round(ms_plain * 1e3, 1),
                     "overhead_pct": round(100.0 * (ms_ck - ms_plain) / ms_plain, 2)}
         del ck
+    # Decode at larger batches: B slots x 1 token over cold pools, as graph
+    # replays, beside a plain device copy of the same state bytes (read B x
+    # 3 MiB, write B x 3 MiB) between cold buffers -- what the memory system
+    # gives a kernel that only streams the state.
+    sweep = None
+    if not args.no_decode_sweep:
+        sweep = []
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        for B in DECODE_SWEEP:
+            gB = gdn.Geometry(n_slots=B)
+            pool_bytes = B * DECODE_STATE_BYTES // 8
+            n_pool = max(2, -(-1_000_000_000 // pool_bytes))  # > 1 GB between reuses of one pool
+            bpools = []
+            for _ in range(n_pool):
+                pl = gdn.SlotPool.zeros(gB)
+                pl.state.normal_(0.0, 0.02, generator=gen)
+                pl.conv_state.normal_(0.0, 0.1, generator=gen)
+                bpools.append(pl)
+            bx = torch.randn(B, g.conv_channels, generator=gen, device=dev).to(bf)
+            ba = torch.randn(B, g.n_v_heads, generator=gen, device=dev).to(bf)
+            bb = torch.randn(B, g.n_v_heads, generator=gen, device=dev).to(bf)
+            bslot = torch.arange(B, dtype=torch.int32, device=dev)
+            bo = torch.empty(B, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+            f_b = lambda i: gdn.decode_step(gB, bpools[i % n_pool], bx, ba, bb, cw, bslot, bo, dev_err=err)
+            ms_b = graph_ms(f_b, 2 * n_pool)
+            del bpools
+            bufs = [torch.empty(pool_bytes // 4, dtype=torch.float32, device=dev) for _ in range(2 * n_pool)]
+            for t in bufs:
+                t.normal_(generator=gen)
+            f_c = lambda i: bufs[(2 * i + 1) % len(bufs)].copy_(bufs[(2 * i) % len(bufs)])
+            f_c(0)
+            ms_c = loop_ms(f_c, 2 * n_pool)
+            del bufs
+            moved = B * (DECODE_BYTES // 4)
+            sweep.append({"slots": B, "us": round(ms_b * 1e3, 2), "gbs": round(moved / (ms_b * 1e-3) / 1e9, 1),
+                          "frac_hbm_peak": round(moved / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "copy_us": round(ms_c * 1e3, 2),
+                          "copy_gbs": round(2 * pool_bytes / (ms_c * 1e-3) / 1e9, 1), "cold_pools": n_pool})
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the decode batch sweep"}))
+            sys.exit(3)
+    # Round economics of speculative decoding at this layer: verify(k) +
+    # rollback in decode steps, k = 1 .. max_draft, 4 slots, graph
+    # replays over cold pools.  The draft head's own cost is not part of this
+    # layer and is left out.
+    econ = None
+    if not args.no_economics:
+        rounds = []
+        for k in range(1, geom.max_draft + 1):
+            vxk, vak, vbk = vx[:, :k].contiguous(), va[:, :k].contiguous(), vb[:, :k].contiguous()
+            snapk = torch.empty(4, k, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+            vok = torch.empty(4, k, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+            f_vk = lambda i: gdn.verify_k(geom, pools[i % len(pools)], vxk, vak, vbk, cw, vslot, snapk, vok,
+                                          dev_err=err)
+            ms_vk = ms_verify if k == 4 else graph_ms(f_vk, n_loop)
+            cost = (ms_vk + ms_rollback) / ms_decode
+            be = break_even_acceptance(cost, k)
+            rounds.append({"k": k, "verify_us": round(ms_vk * 1e3, 2), "round_cost_steps": round(cost, 3),
+                           "break_even_p": None if be is None else round(be, 3),
+                           "speedup_at_p": {str(p_): round(expected_tokens(p_, k) / cost, 3)
+                                            for p_ in (0.65, 0.74, 0.9)}})
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the verify economics"}))
+            sys.exit(3)
+        econ = {"decode_us": round(ms_decode * 1e3, 2), "rollback_us": round(ms_rollback * 1e3, 2),
+                "slots": 4, "cost": "verify(k) + rollback, in decode steps; draft head excluded",
+                "rounds": rounds}
     if min(ms_prefill, ms_decode, ms_verify, ms_step) <= 0:
         print(json.dumps({"error": "a timing came out as zero"}))
         sys.exit(5)
@@ -459,6 +563,8 @@ def main():
                      "timing": "graph replay", "eager_loop_us": round(ms_rollback_eager * 1e3, 2)},
         "prefill_varlen": varlen,
         "prefill_ckpt": ckpt_fig,
+        "decode_batch": sweep,
+        "verify_economics": econ,
         "wall_s": round(wall, 3),
     }
 

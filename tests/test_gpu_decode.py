@@ -65,6 +65,25 @@ def test_decode_workload2_full():
     assert not pool.conv_pos[:, 1:].any()  # the rest of each slot's line is never written
 
 
+def test_decode_batch_64():
+    """64 slots in one call (the batch sweep's middle size) out of a pool of 66:
+    every row's output and state within 2e-2, the two untouched slots bitwise
+    unchanged, every position +1."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_slots=66)
+    inp = gi.decode_inputs(seed=140, geom=g, batch=64)
+    pool, o_gpu, o_ref, st_ref, hi_ref = _run_decode(g, inp)
+    assert H.relerr(o_gpu, o_ref) <= H.TOL_BF16
+    state = pool.state.cpu().numpy()
+    for s in range(g.n_slots):
+        if s in inp["slots"]:
+            assert H.relerr(state[s], st_ref[s]) <= H.TOL_BF16, f"slot {s}"
+        else:
+            assert np.array_equal(state[s], inp["state"][s]), f"untouched slot {s} changed"
+    assert np.array_equal(H.read_hist(g, pool), hi_ref.astype(np.float32))
+    pos = H.positions(pool)
+    assert all(pos[s] == inp["pos"][s] + (1 if s in inp["slots"] else 0) for s in range(g.n_slots))
+
+
 def test_decode_tight_error_bound():
     """The achieved error is far inside the gate (fp32 state, fp32 math)."""
     inp = gi.workload(2, seed=7)
