@@ -524,6 +524,38 @@ def main():
         econ = {"decode_us": round(ms_decode * 1e3, 2), "rollback_us": round(ms_rollback * 1e3, 2),
                 "slots": 4, "cost": "verify(k) + rollback, in decode steps; draft head excluded",
                 "rounds": rounds}
+        # The same k = 4 round with zero-copy commit: verify into pool slots
+        # (each snapshot a whole slot) and a commit that only picks slot ids.
+        gz = gdn.Geometry(n_slots=24)
+        nz = 8  # 8 pools of 24 slots (600 MB): every call finds its pool cold
+        zpools = []
+        for _ in range(nz):
+            pl = gdn.SlotPool.zeros(gz)
+            pl.state.normal_(0.0, 0.02)
+            pl.conv_state.normal_(0.0, 0.1)
+            zpools.append(pl)
+        zslot = torch.arange(4, dtype=torch.int32, device=dev)
+        zss = torch.arange(4, 20, dtype=torch.int32, device=dev).view(4, 4)
+        znext = torch.empty(4, dtype=torch.int32, device=dev)
+        f_vz = lambda i: gdn.verify_k_slots(gz, zpools[i % nz], vx, va, vb, cw, zslot, zss, vo, dev_err=err)
+        f_cz = lambda i: gdn.commit_slots(gz, zslot, zss, vacc, znext, dev_err=err)
+        ms_vz = graph_ms(f_vz, 2 * nz)
+        ms_cz = graph_ms(f_cz, n_loop)
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the zero-copy round"}))
+            sys.exit(3)
+        # the copy path when every row accepts all 4 drafts (4 state copies)
+        acc_all = torch.full((4,), 4, dtype=torch.int32, device=dev)
+        f_rall = lambda i: gdn.rollback(geom, pools[i % len(pools)], snap, vslot, acc_all, dev_err=err)
+        ms_rall = graph_ms(f_rall, n_loop)
+        cost_z = (ms_vz + ms_cz) / ms_decode
+        be_z = break_even_acceptance(cost_z, 4)
+        econ["zero_copy_k4"] = {"verify_slots_us": round(ms_vz * 1e3, 2), "commit_us": round(ms_cz * 1e3, 2),
+                                "round_cost_steps": round(cost_z, 3),
+                                "break_even_p": None if be_z is None else round(be_z, 3),
+                                "copy_path_rollback_all_accepted_us": round(ms_rall * 1e3, 2),
+                                "copy_path_round_all_accepted_steps": round((ms_verify + ms_rall) / ms_decode, 3)}
+        del zpools
     # A stack of GDN layers (each its own slot pool, conv weights and inputs),
     # 4 slots: one decode token through every layer, and one verify(4) +
     # rollback round through every layer, each captured as one HIP graph and

@@ -78,6 +78,9 @@ _SIGS = {
     "gdn_verify_k": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
                                     _P, _P, _P, _P]),
     "gdn_rollback": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _I, _P, _P]),
+    "gdn_verify_k_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                          _P, _P, _P, _P]),
+    "gdn_commit_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _I, _I, _P, _P, _P]),
 }
 
 _lib = None
@@ -263,6 +266,39 @@ def rollback(geom: Geometry, pool: SlotPool, snap, slot, accepted, dev_err=None,
                               _ptr(accepted), B, k, _ptr(dev_err), _stream(stream)))
 
 
+def verify_k_slots(geom: Geometry, pool: SlotPool, x, a, b, conv_w, slot, snap_slot, o, dev_err=None,
+                   stream=None):
+    """gdn_verify_k_slots: as verify_k, but snapshot j of row i becomes pool slot snap_slot[i][j]."""
+    B, k = x.shape[0], x.shape[1]
+    C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
+    _check_pool(geom, pool)
+    _need(x, "x", (B, k, C), geom.dtype)
+    _need(a, "a", (B, k, Hv), geom.dtype)
+    _need(b, "b", (B, k, Hv), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
+    _need(slot, "slot", (B,), torch.int32)
+    _need(snap_slot, "snap_slot", (B, k), torch.int32)
+    _need(o, "o", (B, k, Hv, dv), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_verify_k_slots(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
+                                    _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(slot), B,
+                                    k, _ptr(snap_slot), _ptr(o), _ptr(dev_err), _stream(stream)))
+
+
+def commit_slots(geom: Geometry, slot, snap_slot, accepted, next_slot, dev_err=None, stream=None):
+    """gdn_commit_slots: next_slot[i] = snap_slot[i][accepted[i]-1], or slot[i] when accepted[i] == 0."""
+    B, k = snap_slot.shape[0], snap_slot.shape[1]
+    _need(slot, "slot", (B,), torch.int32)
+    _need(snap_slot, "snap_slot", (B, k), torch.int32)
+    _need(accepted, "accepted", (B,), torch.int32)
+    _need(next_slot, "next_slot", (B,), torch.int32)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    g = geom.c_struct()
+    _check(lib().gdn_commit_slots(ctypes.byref(g), _ptr(slot), _ptr(snap_slot), _ptr(accepted), B, k,
+                                  _ptr(next_slot), _ptr(dev_err), _stream(stream)))
+
+
 def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_seqs: int) -> int:
     g = geom.c_struct()
     return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(g), n_tokens, n_seqs))
@@ -328,7 +364,7 @@ def checkpoint_count(seq_lens, ckpt_every: int) -> int:
 
 __all__ = [
     "Geometry", "GdnGeometry", "GdnError", "SlotPool", "lib", "conv_state_step", "decode_step", "verify_k",
-    "rollback", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
+    "rollback", "verify_k_slots", "commit_slots", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
     "checkpoint_count", "POS_ONE", "CHUNK",
     "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS",
 ]

@@ -285,6 +285,70 @@ gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_s
   return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k");
 }
 
+gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                              const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                              const int32_t* slot, int32_t batch, int32_t k, const int32_t* snap_slot, void* o,
+                              int32_t* dev_err, void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  if (k < 1 || k > g->max_draft)
+    return fail(GDN_ERR_RANGE, "k: %d, required: 1..max_draft = %d", k, g->max_draft);
+  if (static_cast<int64_t>(batch) * (k + 1) > g->n_slots)
+    return fail(GDN_ERR_RANGE, "batch * (k + 1): %lld, required: <= n_slots = %d (rows and snapshots need distinct slots)",
+                static_cast<long long>(batch) * (k + 1), g->n_slots);
+  GDN_NEED_PTR(state, "state");
+  if (g->conv_width > 0) {
+    GDN_NEED_PTR(conv_state, "conv_state");
+    GDN_NEED_PTR4(conv_pos, "conv_pos");
+    GDN_NEED_PTR(conv_w, "conv_w");
+  }
+  GDN_NEED_PTR(x, "x");
+  GDN_NEED_PTR(a_in, "a");
+  GDN_NEED_PTR(b_in, "b");
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR4(snap_slot, "snap_slot");
+  GDN_NEED_PTR(o, "o");
+  gdn::StepArgs a = step_args(g);
+  a.state = state;
+  a.conv_state = conv_state;
+  a.conv_pos = conv_pos;
+  a.x = x;
+  a.a = a_in;
+  a.b = b_in;
+  a.conv_w = conv_w;
+  a.slot = slot;
+  a.snap_slot = snap_slot;
+  a.o = o;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = k;
+  return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k_slots");
+}
+
+gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* snap_slot,
+                            const int32_t* accepted, int32_t batch, int32_t k, int32_t* next_slot,
+                            int32_t* dev_err, void* stream) {
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  if ((s = check_batch(batch, g)) != GDN_OK) return s;
+  if (k < 1 || k > g->max_draft)
+    return fail(GDN_ERR_RANGE, "k: %d, required: 1..max_draft = %d", k, g->max_draft);
+  GDN_NEED_PTR4(slot, "slot");
+  GDN_NEED_PTR4(snap_slot, "snap_slot");
+  GDN_NEED_PTR4(accepted, "accepted");
+  GDN_NEED_PTR4(next_slot, "next_slot");
+  gdn::StepArgs a = step_args(g);
+  a.slot = slot;
+  a.snap_slot = snap_slot;
+  a.accepted = accepted;
+  a.next_slot = next_slot;
+  a.dev_err = dev_err;
+  a.batch = batch;
+  a.k = k;
+  return launched(gdn::launch_commit_slots(a, stream), "gdn_commit_slots");
+}
+
 gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos, const float* snap,
                         const int32_t* slot, const int32_t* accepted, int32_t batch, int32_t k, int32_t* dev_err,
                         void* stream) {

@@ -22,6 +22,8 @@ struct StepArgs {
   const int32_t* accepted;  // rollback only
   void* o;                  // o, or y for the conv step
   float* snap;              // verify: out; rollback: in
+  const int32_t* snap_slot; // verify into pool slots: [batch][k] slots receiving the snapshots (else null)
+  int32_t* next_slot;       // slot commit: out
   int32_t* dev_err;
   int32_t batch, k;
   int32_t Hk, Hv, D, C, W, R, n_slots;
@@ -70,6 +72,7 @@ int launch_decode(const StepArgs& a, bool bf16, void* stream);
 int launch_verify(const StepArgs& a, bool bf16, void* stream);
 int launch_conv_step(const StepArgs& a, bool bf16, void* stream);
 int launch_rollback(const StepArgs& a, void* stream);
+int launch_commit_slots(const StepArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, bool bf16, void* stream);
 
 }  // namespace gdn

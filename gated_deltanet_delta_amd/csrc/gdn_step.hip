@@ -201,8 +201,19 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
   const bool qk_writer = fe_qk && (h % G == 0) && hb == 0 && slot_ok;
   const bool v_writer = fe_v && slot_ok;
   const bool o_writer = (lane % LPR) == 0 && slot_ok;
+  // Verify into pool slots: snapshot j becomes a whole slot (state, conv
+  // history, position) of its own, so a commit only has to pick a slot id.
+  const bool to_slots = VERIFY && A.snap_slot != nullptr;
 
   for (int j = 0; j < kdr; ++j) {
+    int ss = 0;
+    bool ss_ok = false;
+    if (to_slots) {
+      const int ss_in = A.snap_slot[static_cast<size_t>(b) * kdr + j];
+      ss_ok = slot_ok && ss_in >= 0 && ss_in < A.n_slots;
+      if (!ss_ok && slot_ok && tid == 0 && blockIdx.x == 0) report_error(A.dev_err, GDN_DEV_BAD_SLOT);
+      ss = ss_ok ? ss_in : 0;
+    }
     // next draft's inputs (verify), requested before this draft's arithmetic
     float nxq = xq, nxv = xv, na = ga, nb = gb;
     if (VERIFY && j + 1 < kdr) {
@@ -219,6 +230,18 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
       yv = silu_fast(fmaf(wv.w, xv, fmaf(wv.z, hv[2], fmaf(wv.y, hv[1], wv.x * hv[0]))));
       hq[0] = hq[1]; hq[1] = hq[2]; hq[2] = xq;
       hv[0] = hv[1]; hv[1] = hv[2]; hv[2] = xv;
+      if (to_slots && ss_ok) {
+        // the snapshot slot's history: tokens pos+j-2 .. pos+j, at their ring rows
+        float* sring = A.conv_state + static_cast<size_t>(ss) * R * C;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          float* rr = sring + static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(j + t) - 2u, R)) * C;
+          if (qk_writer) rr[chq] = hq[t];
+          if (v_writer) rr[chv] = hv[t];
+        }
+        if (h == 0 && hb == 0 && tid == 0)
+          A.conv_pos[ss * kPosStride] = static_cast<int32_t>((pos + static_cast<uint32_t>(j + 1)) << kPosShift);
+      }
     } else {
       yq = xq;
       yv = xv;
@@ -288,10 +311,12 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
       S[p] = sn;
       if (!VERIFY && slot_ok)
         store_nt4(A.state + (static_cast<size_t>(slot) * A.Hv + h) * D * D + static_cast<size_t>(row) * D + c4, sn);
-      if (VERIFY && slot_ok) {
+      if (VERIFY && slot_ok && !to_slots) {
         float* dst = A.snap + ((((static_cast<size_t>(b) * kdr + j) * A.Hv + h) * D + row) * D + c4);
         store_nt4(dst, sn);
       }
+      if (to_slots && ss_ok)
+        store_nt4(A.state + (static_cast<size_t>(ss) * A.Hv + h) * D * D + static_cast<size_t>(row) * D + c4, sn);
       if (o_writer) store_out<BF16>(A.o, (gi * D) + row, ov);
     }
     xq = nxq;
@@ -361,6 +386,19 @@ __global__ __launch_bounds__(256) void rollback_kernel(StepArgs A) {
                                             (static_cast<uint32_t>(n) << kPosShift));
 }
 
+// Commit after a verify into pool slots: the row's sequence continues in the
+// slot that holds the state after its last accepted draft (its own slot when
+// none was accepted).  Nothing is copied.
+__global__ __launch_bounds__(256) void commit_slots_kernel(StepArgs A) {
+  for (int b = blockIdx.x * 256 + threadIdx.x; b < A.batch; b += gridDim.x * 256) {
+    const int n = A.accepted[b];
+    int out = A.slot[b];
+    if (n < 0 || n > A.k) report_error(A.dev_err, GDN_DEV_BAD_ACCEPTED);
+    else if (n > 0) out = A.snap_slot[static_cast<size_t>(b) * A.k + (n - 1)];
+    A.next_slot[b] = out;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -396,6 +434,13 @@ int launch_conv_step(const StepArgs& a, bool bf16, void* stream) {
   if (a.W != 4) return static_cast<int>(hipErrorInvalidValue);
   if (bf16) hipLaunchKernelGGL((conv_step_kernel<true, 4>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((conv_step_kernel<false, 4>), grid, dim3(256), 0, s, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_commit_slots(const StepArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int wgs = (a.batch + 255) / 256;
+  hipLaunchKernelGGL(commit_slots_kernel, dim3(wgs < 64 ? wgs : 64), dim3(256), 0, s, a);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -268,6 +268,42 @@ gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos,
                         const float* snap, const int32_t* slot, const int32_t* accepted,
                         int32_t batch, int32_t k, int32_t* dev_err, void* stream);
 
+/*
+ * Verify with zero-copy commit ("Forge", entry of 27 August: a snapshot of
+ * the state after every draft row makes rollback a copy; here the snapshot
+ * is a whole pool slot, so the commit copies nothing).  Computes exactly what
+ * gdn_verify_k computes, bit for bit, but snapshot j of row i goes to pool
+ * slot s_j = snap_slot[i][j] (device int32 [batch][k]) as a complete slot:
+ *   state[s_j]      = state after draft j (fp32, as snap[i][j] of gdn_verify_k),
+ *   conv ring of s_j = the W-1 inputs before position p+j+1 (committed history
+ *                      and drafts), at their ring rows,
+ *   conv_pos[s_j]   = p+j+1 tokens,
+ * where p is slot[i]'s position.  slot[i]'s state and position are not
+ * modified; its ring receives the drafts' inputs as in gdn_verify_k.  Any
+ * earlier contents of the snapshot slots are overwritten.
+ * Every slot id in slot[] and snap_slot[] must be distinct (undefined results
+ * otherwise); a snapshot slot id out of range sets GDN_DEV_BAD_SLOT and that
+ * snapshot is skipped.  batch * (k+1) <= n_slots.  A caller that verifies the
+ * last accepted token together with its drafts passes them as k+1 rows.
+ */
+gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_state,
+                              int32_t* conv_pos, const void* x, const void* a, const void* b,
+                              const float* conv_w, const int32_t* slot, int32_t batch, int32_t k,
+                              const int32_t* snap_slot, void* o, int32_t* dev_err, void* stream);
+
+/*
+ * Commit after gdn_verify_k_slots (same slot, snap_slot, batch and k): for
+ * each row with n = accepted[i] (device int32 [batch], 0..k),
+ *   next_slot[i] = snap_slot[i][n-1] if n >= 1, else slot[i]   (device int32 [batch]).
+ * The row's sequence continues in next_slot[i]; nothing is copied.  The
+ * other slots of the row (slot[i] when n >= 1, and the snapshot slots not
+ * chosen) hold nothing the sequence needs any more.  An accepted length out
+ * of range sets GDN_DEV_BAD_ACCEPTED and keeps slot[i].
+ */
+gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* snap_slot,
+                            const int32_t* accepted, int32_t batch, int32_t k, int32_t* next_slot,
+                            int32_t* dev_err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

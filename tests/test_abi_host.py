@@ -184,6 +184,25 @@ def test_prefill_checkpoint_refusals(gdn):
     assert st == 1 and "state: NULL" in L.gdn_last_error().decode()
 
 
+def test_verify_slots_and_commit_refusals(gdn):
+    L = gdn.lib()
+    g = _geom(gdn, n_slots=20)
+    va = lambda batch, k, ss=_p(): [ctypes.byref(g)] + [_p()] * 8 + [batch, k, ss, _p(), None, None]  # noqa: E731
+    assert L.gdn_verify_k_slots(*va(4, 5)) == 5
+    assert "k: 5, required: 1..max_draft = 4" in L.gdn_last_error().decode()
+    g.n_slots = 19
+    assert L.gdn_verify_k_slots(*va(4, 4)) == 5
+    assert "batch * (k + 1): 20, required: <= n_slots = 19" in L.gdn_last_error().decode()
+    g.n_slots = 20
+    assert L.gdn_verify_k_slots(*va(4, 4, None)) == 1
+    assert "snap_slot: NULL" in L.gdn_last_error().decode()
+    cm = [ctypes.byref(g), _p(), _p(), _p(), 4, 4, None, None, None]
+    assert L.gdn_commit_slots(*cm) == 1
+    assert "next_slot: NULL" in L.gdn_last_error().decode()
+    cm = [ctypes.byref(g), _p(), _p(), _p(), 0, 4, _p(), None, None]
+    assert L.gdn_commit_slots(*cm) == 5
+
+
 def test_conv_step_refusals(gdn):
     L = gdn.lib()
     g = _geom(gdn, conv_width=0)

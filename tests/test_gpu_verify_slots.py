@@ -1,0 +1,167 @@
+"""Verify into pool slots and zero-copy commit, on the GPU: every snapshot is
+a whole slot (state, conv history, position); the commit only picks a slot
+id.  Checked against the oracle and bit for bit against verify + rollback."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import harness as H
+from oracle import gdn_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _gdn():
+    import gated_deltanet_delta_amd as gdn
+    gdn.lib()
+    return gdn
+
+
+def _snap_slots(g, slots, k):
+    """Distinct pool slots for the snapshots: the ones no row uses, in order."""
+    free = [s for s in range(g.n_slots) if s not in set(int(x) for x in slots)]
+    assert len(free) >= len(slots) * k
+    return np.array(free[:len(slots) * k], np.int32).reshape(len(slots), k)
+
+
+def _run_both(g, inp, k, accepted):
+    """The copy path (verify + rollback) on one pool, the slot path (verify
+    into slots + commit) on an identical pool."""
+    gdn = _gdn()
+    geom = H.to_geom(g)
+    dt = H.in_dtype(g)
+    B = len(inp["slots"])
+    x, a, b = (H.dev(inp[n][:, :k], dt) for n in ("x", "a", "b"))
+    cw = H.dev(inp["conv_w"])
+    slot = H.dev(inp["slots"])
+    acc = H.dev(np.asarray(accepted, np.int32))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+    snap = torch.empty(B, k, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device="cuda")
+    oa = torch.empty(B, k, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
+    gdn.verify_k(geom, pa, x, a, b, cw, slot, snap, oa, dev_err=err)
+    gdn.rollback(geom, pa, snap, slot, acc, dev_err=err)
+    pb = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+    ss = _snap_slots(g, inp["slots"], k)
+    ob = torch.empty_like(oa)
+    nxt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    gdn.verify_k_slots(geom, pb, x, a, b, cw, slot, H.dev(ss), ob, dev_err=err)
+    gdn.commit_slots(geom, slot, H.dev(ss), acc, nxt, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return pa, snap, oa, pb, ss, ob, nxt
+
+
+def test_verify_slots_equals_the_copy_path():
+    """4 rows x k = 4 with accepted 0..4: outputs, every snapshot slot, and the
+    committed slot's state, history and position equal verify + rollback bit
+    for bit, and the oracle within 2e-2; a decode step then continues both
+    paths identically."""
+    gdn = _gdn()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_slots=24)
+    inp = gi.verify_inputs(seed=710, geom=g, batch=4, k=4)
+    k = 4
+    accepted = [0, 1, 4, 2]
+    pa, snap, oa, pb, ss, ob, nxt = _run_both(g, inp, k, accepted)
+    assert torch.equal(oa, ob)
+    hist_b = H.read_hist(g, pb)
+    pos_b = H.positions(pb)
+    for i, s in enumerate(inp["slots"]):
+        p0 = int(inp["pos"][s])
+        o_r, snaps_r, hists_r = orc.verify(g, inp["state"][s], inp["hist"][s], inp["x"][i, :k], inp["a"][i, :k],
+                                           inp["b"][i, :k], inp["conv_w"])
+        for j in range(k):
+            sj = int(ss[i, j])
+            assert torch.equal(pb.state[sj], snap[i, j]), f"row {i} snapshot {j} differs from verify_k's"
+            assert H.relerr(pb.state[sj].cpu().numpy(), snaps_r[j]) <= H.TOL_BF16
+            assert np.array_equal(hist_b[sj], hists_r[j].astype(np.float32)), f"row {i} snapshot {j} history"
+            assert pos_b[sj] == p0 + j + 1
+        # the row's own slot keeps its state and position
+        assert torch.equal(pb.state[s], torch.from_numpy(inp["state"][s]).cuda())
+        assert pos_b[s] == p0
+    nxt_h = nxt.cpu().numpy()
+    hist_a = H.read_hist(g, pa)
+    pos_a = H.positions(pa)
+    for i, s in enumerate(inp["slots"]):
+        n = accepted[i]
+        want = int(s) if n == 0 else int(ss[i, n - 1])
+        assert nxt_h[i] == want
+        assert torch.equal(pb.state[want], pa.state[s])
+        assert np.array_equal(hist_b[want], hist_a[s])
+        assert pos_b[want] == pos_a[s]
+    # one more token through both: bit-identical outputs and states
+    geom = H.to_geom(g)
+    dt = H.in_dtype(g)
+    rng = np.random.Generator(np.random.PCG64(711))
+    dx = H.dev(rng.normal(size=(4, g.conv_channels)).astype(np.float32), dt)
+    da = H.dev(rng.normal(size=(4, g.n_v_heads)).astype(np.float32), dt)
+    db = H.dev(rng.normal(size=(4, g.n_v_heads)).astype(np.float32), dt)
+    cw = H.dev(inp["conv_w"])
+    o1 = torch.empty(4, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
+    o2 = torch.empty_like(o1)
+    gdn.decode_step(geom, pa, dx, da, db, cw, H.dev(inp["slots"]), o1)
+    gdn.decode_step(geom, pb, dx, da, db, cw, nxt, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for i, s in enumerate(inp["slots"]):
+        assert torch.equal(pa.state[s], pb.state[int(nxt_h[i])])
+
+
+@pytest.mark.parametrize("accepted", [[1, 5, 3], [5, 1, 2]])
+def test_verify_slots_k_plus_one_rows(accepted):
+    """The last accepted token verified with its 4 drafts as k + 1 = 5 rows
+    (max_draft 5): at least the first row is always accepted; the committed
+    slot holds the oracle's state and history after those rows."""
+    gdn = _gdn()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=4, n_v_heads=12, n_slots=20, max_draft=5)
+    k = 5
+    inp = gi.verify_inputs(seed=720 + accepted[0], geom=g, batch=3, k=k)
+    pa, snap, oa, pb, ss, ob, nxt = _run_both(g, inp, k, accepted)
+    hist_b = H.read_hist(g, pb)
+    pos_b = H.positions(pb)
+    nxt_h = nxt.cpu().numpy()
+    for i, s in enumerate(inp["slots"]):
+        o_r, snaps_r, hists_r = orc.verify(g, inp["state"][s], inp["hist"][s], inp["x"][i], inp["a"][i],
+                                           inp["b"][i], inp["conv_w"])
+        assert H.relerr(H.f64(ob[i]), o_r) <= H.TOL_BF16
+        n = accepted[i]
+        S_r, h_r = orc.rollback(inp["state"][s], inp["hist"][s], snaps_r, hists_r, n)
+        t = int(nxt_h[i])
+        assert t == int(ss[i, n - 1])
+        assert H.relerr(pb.state[t].cpu().numpy(), S_r) <= H.TOL_BF16
+        assert np.array_equal(hist_b[t], h_r.astype(np.float32))
+        assert pos_b[t] == int(inp["pos"][s]) + n
+        assert torch.equal(pb.state[t], pa.state[s])
+
+
+def test_verify_slots_bad_ids_reported():
+    """A snapshot slot id out of range sets GDN_DEV_BAD_SLOT and only that
+    snapshot is skipped; an accepted length out of range sets
+    GDN_DEV_BAD_ACCEPTED and keeps the row's own slot."""
+    gdn = _gdn()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=12)
+    k = 2
+    inp = gi.verify_inputs(seed=730, geom=g, batch=2, k=k)
+    geom = H.to_geom(g)
+    dt = H.in_dtype(g)
+    pool = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+    ss = _snap_slots(g, inp["slots"], k)
+    good = int(ss[1, 1])
+    ss[0, 1] = g.n_slots + 7
+    before = pool.state.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty(2, k, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
+    gdn.verify_k_slots(geom, pool, *(H.dev(inp[n][:, :k], dt) for n in ("x", "a", "b")), H.dev(inp["conv_w"]),
+                       H.dev(inp["slots"]), H.dev(ss), o, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == gdn.DEV_BAD_SLOT
+    assert not torch.equal(pool.state[good], before[good])  # the valid snapshots were written
+    err.zero_()
+    nxt = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    gdn.commit_slots(geom, H.dev(inp["slots"]), H.dev(ss), H.dev(np.array([k + 1, 1], np.int32)), nxt, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == gdn.DEV_BAD_ACCEPTED
+    assert nxt.cpu().tolist() == [int(inp["slots"][0]), int(ss[1, 0])]
