@@ -30,6 +30,8 @@ DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
 DEV_BAD_SEQLENS = 3
+DEV_WAIT_TIMEOUT = 4
+DEV_BAD_K = 5
 
 
 class GdnGeometry(ctypes.Structure):
@@ -79,8 +81,8 @@ _SIGS = {
                                     _P, _P, _P, _P]),
     "gdn_rollback": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _I, _P, _P]),
     "gdn_verify_k_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
-                                          _P, _P, _P, _P]),
-    "gdn_commit_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _I, _I, _P, _P, _P]),
+                                          _P, _P, _P, _P, _P]),
+    "gdn_commit_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _I, _I, _P, _P, _P]),
 }
 
 _lib = None
@@ -267,8 +269,9 @@ def rollback(geom: Geometry, pool: SlotPool, snap, slot, accepted, dev_err=None,
 
 
 def verify_k_slots(geom: Geometry, pool: SlotPool, x, a, b, conv_w, slot, snap_slot, o, dev_err=None,
-                   stream=None):
-    """gdn_verify_k_slots: as verify_k, but snapshot j of row i becomes pool slot snap_slot[i][j]."""
+                   stream=None, k_row=None):
+    """gdn_verify_k_slots: as verify_k, but snapshot j of row i becomes pool slot snap_slot[i][j];
+    k_row (device int32 [batch], optional) gives each row its own number of drafts."""
     B, k = x.shape[0], x.shape[1]
     C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
     _check_pool(geom, pool)
@@ -278,25 +281,27 @@ def verify_k_slots(geom: Geometry, pool: SlotPool, x, a, b, conv_w, slot, snap_s
     _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
     _need(slot, "slot", (B,), torch.int32)
     _need(snap_slot, "snap_slot", (B, k), torch.int32)
+    _need(k_row, "k_row", (B,), torch.int32, optional=True)
     _need(o, "o", (B, k, Hv, dv), geom.dtype)
     _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
     g = geom.c_struct()
     _check(lib().gdn_verify_k_slots(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
                                     _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(slot), B,
-                                    k, _ptr(snap_slot), _ptr(o), _ptr(dev_err), _stream(stream)))
+                                    k, _ptr(k_row), _ptr(snap_slot), _ptr(o), _ptr(dev_err), _stream(stream)))
 
 
-def commit_slots(geom: Geometry, slot, snap_slot, accepted, next_slot, dev_err=None, stream=None):
+def commit_slots(geom: Geometry, slot, snap_slot, accepted, next_slot, dev_err=None, stream=None, k_row=None):
     """gdn_commit_slots: next_slot[i] = snap_slot[i][accepted[i]-1], or slot[i] when accepted[i] == 0."""
     B, k = snap_slot.shape[0], snap_slot.shape[1]
     _need(slot, "slot", (B,), torch.int32)
+    _need(k_row, "k_row", (B,), torch.int32, optional=True)
     _need(snap_slot, "snap_slot", (B, k), torch.int32)
     _need(accepted, "accepted", (B,), torch.int32)
     _need(next_slot, "next_slot", (B,), torch.int32)
     _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
     g = geom.c_struct()
-    _check(lib().gdn_commit_slots(ctypes.byref(g), _ptr(slot), _ptr(snap_slot), _ptr(accepted), B, k,
-                                  _ptr(next_slot), _ptr(dev_err), _stream(stream)))
+    _check(lib().gdn_commit_slots(ctypes.byref(g), _ptr(slot), _ptr(k_row), _ptr(snap_slot), _ptr(accepted), B,
+                                  k, _ptr(next_slot), _ptr(dev_err), _stream(stream)))
 
 
 def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_seqs: int) -> int:
@@ -366,5 +371,5 @@ __all__ = [
     "Geometry", "GdnGeometry", "GdnError", "SlotPool", "lib", "conv_state_step", "decode_step", "verify_k",
     "rollback", "verify_k_slots", "commit_slots", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
     "checkpoint_count", "POS_ONE", "CHUNK",
-    "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS",
+    "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS", "DEV_WAIT_TIMEOUT", "DEV_BAD_K",
 ]

@@ -287,8 +287,8 @@ gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_s
 
 gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
                               const void* x, const void* a_in, const void* b_in, const float* conv_w,
-                              const int32_t* slot, int32_t batch, int32_t k, const int32_t* snap_slot, void* o,
-                              int32_t* dev_err, void* stream) {
+                              const int32_t* slot, int32_t batch, int32_t k, const int32_t* k_row,
+                              const int32_t* snap_slot, void* o, int32_t* dev_err, void* stream) {
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   if ((s = check_batch(batch, g)) != GDN_OK) return s;
@@ -319,6 +319,8 @@ gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_s
   a.conv_w = conv_w;
   a.slot = slot;
   a.snap_slot = snap_slot;
+  if (k_row) GDN_NEED_PTR4(k_row, "k_row");
+  a.k_row = k_row;
   a.o = o;
   a.dev_err = dev_err;
   a.batch = batch;
@@ -326,9 +328,9 @@ gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_s
   return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k_slots");
 }
 
-gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* snap_slot,
-                            const int32_t* accepted, int32_t batch, int32_t k, int32_t* next_slot,
-                            int32_t* dev_err, void* stream) {
+gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* k_row,
+                            const int32_t* snap_slot, const int32_t* accepted, int32_t batch, int32_t k,
+                            int32_t* next_slot, int32_t* dev_err, void* stream) {
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   if ((s = check_batch(batch, g)) != GDN_OK) return s;
@@ -341,6 +343,8 @@ gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const in
   gdn::StepArgs a = step_args(g);
   a.slot = slot;
   a.snap_slot = snap_slot;
+  if (k_row) GDN_NEED_PTR4(k_row, "k_row");
+  a.k_row = k_row;
   a.accepted = accepted;
   a.next_slot = next_slot;
   a.dev_err = dev_err;

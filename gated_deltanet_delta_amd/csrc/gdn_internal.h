@@ -23,6 +23,7 @@ struct StepArgs {
   void* o;                  // o, or y for the conv step
   float* snap;              // verify: out; rollback: in
   const int32_t* snap_slot; // verify into pool slots: [batch][k] slots receiving the snapshots (else null)
+  const int32_t* k_row;     // verify into pool slots, commit: drafts of each row (null: k for every row)
   int32_t* next_slot;       // slot commit: out
   int32_t* dev_err;
   int32_t batch, k;

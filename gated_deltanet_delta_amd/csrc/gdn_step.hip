@@ -204,8 +204,20 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
   // Verify into pool slots: snapshot j becomes a whole slot (state, conv
   // history, position) of its own, so a commit only has to pick a slot id.
   const bool to_slots = VERIFY && A.snap_slot != nullptr;
+  // drafts of this row: k, or the row's own count (rows j >= kn of x, a, b
+  // are not read, and their outputs and snapshots are not written)
+  int kn = kdr;
+  if (VERIFY && A.k_row != nullptr) {
+    const int kr = A.k_row[b];
+    if (kr < 1 || kr > kdr) {
+      if (tid == 0 && blockIdx.x == 0) report_error(A.dev_err, GDN_DEV_BAD_K);
+      kn = 0;
+    } else {
+      kn = kr;
+    }
+  }
 
-  for (int j = 0; j < kdr; ++j) {
+  for (int j = 0; j < kn; ++j) {
     int ss = 0;
     bool ss_ok = false;
     if (to_slots) {
@@ -216,7 +228,7 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
     }
     // next draft's inputs (verify), requested before this draft's arithmetic
     float nxq = xq, nxv = xv, na = ga, nb = gb;
-    if (VERIFY && j + 1 < kdr) {
+    if (VERIFY && j + 1 < kn) {
       nxq = load_in<BF16>(xb + (j + 1) * xrow, chq);
       nxv = load_in<BF16>(xb + (j + 1) * xrow, chv);
       na = load_in<BF16>(A.a, gi + A.Hv);
@@ -392,8 +404,10 @@ __global__ __launch_bounds__(256) void rollback_kernel(StepArgs A) {
 __global__ __launch_bounds__(256) void commit_slots_kernel(StepArgs A) {
   for (int b = blockIdx.x * 256 + threadIdx.x; b < A.batch; b += gridDim.x * 256) {
     const int n = A.accepted[b];
+    const int kr = A.k_row != nullptr ? A.k_row[b] : A.k;
     int out = A.slot[b];
-    if (n < 0 || n > A.k) report_error(A.dev_err, GDN_DEV_BAD_ACCEPTED);
+    if (kr < 1 || kr > A.k) report_error(A.dev_err, GDN_DEV_BAD_K);
+    else if (n < 0 || n > kr) report_error(A.dev_err, GDN_DEV_BAD_ACCEPTED);
     else if (n > 0) out = A.snap_slot[static_cast<size_t>(b) * A.k + (n - 1)];
     A.next_slot[b] = out;
   }

@@ -103,6 +103,7 @@ typedef enum gdn_status {
 #define GDN_DEV_BAD_ACCEPTED 2   /* accepted length outside [0, k] */
 #define GDN_DEV_BAD_SEQLENS 3    /* cu_seqlens[0] != 0, decreasing, or last != n_tokens */
 #define GDN_DEV_WAIT_TIMEOUT 4   /* prefill: a chunk's operands were not published in time; outputs invalid */
+#define GDN_DEV_BAD_K 5          /* a row's draft count outside [1, k] */
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
@@ -285,24 +286,31 @@ gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos,
  * otherwise); a snapshot slot id out of range sets GDN_DEV_BAD_SLOT and that
  * snapshot is skipped.  batch * (k+1) <= n_slots.  A caller that verifies the
  * last accepted token together with its drafts passes them as k+1 rows.
+ * Rows may verify different numbers of drafts: k_row (device int32 [batch],
+ * or NULL for k on every row) gives row i's count k_i in 1..k; x, a, b and o
+ * keep their [batch][k] layout, and rows j >= k_i are neither read nor
+ * written, nor are snap_slot[i][j] for j >= k_i.  A count out of range sets
+ * GDN_DEV_BAD_K and the row is skipped.
  */
 gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_state,
                               int32_t* conv_pos, const void* x, const void* a, const void* b,
                               const float* conv_w, const int32_t* slot, int32_t batch, int32_t k,
-                              const int32_t* snap_slot, void* o, int32_t* dev_err, void* stream);
+                              const int32_t* k_row, const int32_t* snap_slot, void* o,
+                              int32_t* dev_err, void* stream);
 
 /*
- * Commit after gdn_verify_k_slots (same slot, snap_slot, batch and k): for
- * each row with n = accepted[i] (device int32 [batch], 0..k),
+ * Commit after gdn_verify_k_slots (same slot, k_row, snap_slot, batch and k):
+ * for each row with n = accepted[i] (device int32 [batch], 0..k_i),
  *   next_slot[i] = snap_slot[i][n-1] if n >= 1, else slot[i]   (device int32 [batch]).
  * The row's sequence continues in next_slot[i]; nothing is copied.  The
  * other slots of the row (slot[i] when n >= 1, and the snapshot slots not
  * chosen) hold nothing the sequence needs any more.  An accepted length out
- * of range sets GDN_DEV_BAD_ACCEPTED and keeps slot[i].
+ * of range sets GDN_DEV_BAD_ACCEPTED (a draft count out of range,
+ * GDN_DEV_BAD_K) and keeps slot[i].
  */
-gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* snap_slot,
-                            const int32_t* accepted, int32_t batch, int32_t k, int32_t* next_slot,
-                            int32_t* dev_err, void* stream);
+gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* k_row,
+                            const int32_t* snap_slot, const int32_t* accepted, int32_t batch, int32_t k,
+                            int32_t* next_slot, int32_t* dev_err, void* stream);
 
 #ifdef __cplusplus
 }

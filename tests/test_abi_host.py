@@ -187,7 +187,7 @@ def test_prefill_checkpoint_refusals(gdn):
 def test_verify_slots_and_commit_refusals(gdn):
     L = gdn.lib()
     g = _geom(gdn, n_slots=20)
-    va = lambda batch, k, ss=_p(): [ctypes.byref(g)] + [_p()] * 8 + [batch, k, ss, _p(), None, None]  # noqa: E731
+    va = lambda batch, k, ss=_p(): [ctypes.byref(g)] + [_p()] * 8 + [batch, k, None, ss, _p(), None, None]  # noqa: E731
     assert L.gdn_verify_k_slots(*va(4, 5)) == 5
     assert "k: 5, required: 1..max_draft = 4" in L.gdn_last_error().decode()
     g.n_slots = 19
@@ -196,11 +196,15 @@ def test_verify_slots_and_commit_refusals(gdn):
     g.n_slots = 20
     assert L.gdn_verify_k_slots(*va(4, 4, None)) == 1
     assert "snap_slot: NULL" in L.gdn_last_error().decode()
-    cm = [ctypes.byref(g), _p(), _p(), _p(), 4, 4, None, None, None]
+    cm = [ctypes.byref(g), _p(), None, _p(), _p(), 4, 4, None, None, None]
     assert L.gdn_commit_slots(*cm) == 1
     assert "next_slot: NULL" in L.gdn_last_error().decode()
-    cm = [ctypes.byref(g), _p(), _p(), _p(), 0, 4, _p(), None, None]
+    cm = [ctypes.byref(g), _p(), None, _p(), _p(), 0, 4, _p(), None, None]
     assert L.gdn_commit_slots(*cm) == 5
+    # a misaligned per-row count array is refused like any other pointer
+    va_k = [ctypes.byref(g)] + [_p()] * 8 + [4, 4, ctypes.c_void_p(0x10000 + 2), _p(), _p(), None, None]
+    assert L.gdn_verify_k_slots(*va_k) == 2
+    assert "k_row: address" in L.gdn_last_error().decode()
 
 
 def test_conv_step_refusals(gdn):

@@ -165,3 +165,65 @@ def test_verify_slots_bad_ids_reported():
     torch.cuda.synchronize()
     assert int(err.item()) == gdn.DEV_BAD_ACCEPTED
     assert nxt.cpu().tolist() == [int(inp["slots"][0]), int(ss[1, 0])]
+
+
+def test_verify_slots_per_row_k():
+    """Rows verify 4, 1, 3 and 2 drafts in one call: each row's snapshots equal
+    a call of its own with that k, bit for bit, and the oracle within 2e-2;
+    nothing past a row's count is written; the commit picks within each
+    row's count; a count of 0 sets GDN_DEV_BAD_K."""
+    gdn = _gdn()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=4, n_v_heads=12, n_slots=24)
+    geom = H.to_geom(g)
+    dt = H.in_dtype(g)
+    k, kr, acc = 4, [4, 1, 3, 2], [3, 1, 0, 2]
+    inp = gi.verify_inputs(seed=740, geom=g, batch=4, k=k)
+    pool = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+    state0 = pool.state.clone()
+    ss = _snap_slots(g, inp["slots"], k)
+    x, a, b = (H.dev(inp[n], dt) for n in ("x", "a", "b"))
+    cw = H.dev(inp["conv_w"])
+    o = torch.full((4, k, g.n_v_heads, g.d_v), float("nan"), dtype=dt, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nxt = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    gdn.verify_k_slots(geom, pool, x, a, b, cw, H.dev(inp["slots"]), H.dev(ss), o, dev_err=err,
+                       k_row=H.dev(np.array(kr, np.int32)))
+    gdn.commit_slots(geom, H.dev(inp["slots"]), H.dev(ss), H.dev(np.array(acc, np.int32)), nxt, dev_err=err,
+                     k_row=H.dev(np.array(kr, np.int32)))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    hist = H.read_hist(g, pool)
+    pos = H.positions(pool)
+    for i, s in enumerate(inp["slots"]):
+        n = kr[i]
+        o_r, snaps_r, hists_r = orc.verify(g, inp["state"][s], inp["hist"][s], inp["x"][i, :n], inp["a"][i, :n],
+                                           inp["b"][i, :n], inp["conv_w"])
+        assert H.relerr(H.f64(o[i, :n]), o_r) <= H.TOL_BF16
+        assert torch.isnan(o[i, n:].float()).all(), f"row {i}: outputs past its count were written"
+        # the row alone, with its own k, in a pool of its own
+        alone = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+        oa = torch.empty(1, n, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
+        gdn.verify_k_slots(geom, alone, x[i:i + 1, :n].contiguous(), a[i:i + 1, :n].contiguous(),
+                           b[i:i + 1, :n].contiguous(), cw, H.dev(inp["slots"][i:i + 1]),
+                           H.dev(np.ascontiguousarray(ss[i:i + 1, :n])), oa, dev_err=err)
+        torch.cuda.synchronize()
+        assert torch.equal(oa[0], o[i, :n])
+        for j in range(k):
+            sj = int(ss[i, j])
+            if j < n:
+                assert torch.equal(pool.state[sj], alone.state[sj])
+                assert H.relerr(pool.state[sj].cpu().numpy(), snaps_r[j]) <= H.TOL_BF16
+                assert np.array_equal(hist[sj], hists_r[j].astype(np.float32))
+                assert pos[sj] == int(inp["pos"][s]) + j + 1
+            else:
+                assert torch.equal(pool.state[sj], state0[sj]), f"row {i}: snapshot slot {j} past its count"
+        want = int(s) if acc[i] == 0 else int(ss[i, acc[i] - 1])
+        assert int(nxt[i].item()) == want
+    # a count out of range: reported, that row skipped
+    err.zero_()
+    before = pool.state.clone()
+    bad = np.array([0, 1, 1, 1], np.int32)
+    gdn.verify_k_slots(geom, pool, x, a, b, cw, H.dev(inp["slots"]), H.dev(ss), o, dev_err=err, k_row=H.dev(bad))
+    torch.cuda.synchronize()
+    assert int(err.item()) == gdn.DEV_BAD_K
+    assert torch.equal(pool.state[int(ss[0, 0])], before[int(ss[0, 0])])
