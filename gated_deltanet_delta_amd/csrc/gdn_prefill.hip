@@ -1351,7 +1351,10 @@ constexpr int kSegChunks = 16;
 // events per device are created on the first prefill call on that device and
 // kept for the life of the process; the call joins the auxiliary stream back
 // into the caller's stream before it returns, so the caller sees every
-// kernel of the call ordered on its own stream (also under graph capture).
+// kernel of the call ordered on its own stream.  The single-launch form
+// needs the chain and chunk kernels resident at the same time (the chain
+// waits on flags the chunk kernel sets, with a bounded wait), so the prefill
+// is meant for direct launches, not for replay from a captured graph.
 struct AuxStream {
   hipStream_t s = nullptr;
   hipEvent_t ev[8] = {};

@@ -200,7 +200,8 @@ gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_stat
  * so later work on `stream` sees the results.  Calls that share a workspace
  * must be ordered on one stream.  *dev_err receives GDN_DEV_WAIT_TIMEOUT if
  * the internal producer/consumer hand-off ever stalls (the outputs are then
- * not valid).
+ * not valid).  The two kernels of one call must run at the same time, so the
+ * call is made directly on a stream, not captured into a graph.
  */
 gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_state,
                                int32_t* conv_pos, const void* x, const void* a, const void* b,
