@@ -99,6 +99,10 @@ gdn_status check_geometry(const gdn_geometry* g) {
                 g->dtype_in);
   if (g->flags & ~GDN_FLAG_L2NORM_QK)
     return fail(GDN_ERR_GEOMETRY, "flags: 0x%x, required: a subset of GDN_FLAG_L2NORM_QK (0x1)", g->flags);
+  if (g->conv_width == 0 && (g->flags & GDN_FLAG_L2NORM_QK))
+    return fail(GDN_ERR_GEOMETRY,
+                "flags: GDN_FLAG_L2NORM_QK with conv_width: 0, required: no flags (without the conv front end "
+                "x holds q | k | v exactly as the rule uses them)");
   if (!std::isfinite(g->q_scale)) return fail(GDN_ERR_GEOMETRY, "q_scale: %g, required: finite", g->q_scale);
   if (!std::isfinite(g->l2_eps) || g->l2_eps < 0.f)
     return fail(GDN_ERR_GEOMETRY, "l2_eps: %g, required: finite and >= 0", g->l2_eps);

@@ -107,7 +107,7 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
-#define GDN_FLAG_L2NORM_QK 1u    /* L2-normalise q and k after the front end */
+#define GDN_FLAG_L2NORM_QK 1u    /* L2-normalise q and k after the conv front end (requires conv_width > 0) */
 
 /*
  * Geometry of one layer.  Every field is a number some kernel depends on

@@ -53,7 +53,7 @@ def _check(gdn, g):
 
 def test_valid_geometries(gdn):
     assert _check(gdn, _geom(gdn))[0] == 0
-    tiny = _geom(gdn, n_k_heads=1, n_v_heads=1, d_k=16, d_v=16, conv_width=0, n_slots=1)
+    tiny = _geom(gdn, n_k_heads=1, n_v_heads=1, d_k=16, d_v=16, conv_width=0, n_slots=1, l2norm_qk=False)
     tiny.dtype_in = tiny.dtype_out = gdn.GDN_F32
     assert _check(gdn, tiny)[0] == 0
 
@@ -207,9 +207,16 @@ def test_verify_slots_and_commit_refusals(gdn):
     assert "k_row: address" in L.gdn_last_error().decode()
 
 
+def test_norm_without_conv_refused(gdn):
+    """The L2 norm of q and k belongs to the conv front end: without it x holds
+    q | k | v as the rule uses them, and asking for the norm is refused."""
+    st, msg = _check(gdn, _geom(gdn, conv_width=0))
+    assert st == 3 and "GDN_FLAG_L2NORM_QK with conv_width: 0" in msg
+
+
 def test_conv_step_refusals(gdn):
     L = gdn.lib()
-    g = _geom(gdn, conv_width=0)
+    g = _geom(gdn, conv_width=0, l2norm_qk=False)
     assert L.gdn_conv_state_step(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), 4, _p(), None, None) == 3
     assert "conv_width: 0" in L.gdn_last_error().decode()
 

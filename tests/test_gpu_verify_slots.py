@@ -227,3 +227,28 @@ def test_verify_slots_per_row_k():
     torch.cuda.synchronize()
     assert int(err.item()) == gdn.DEV_BAD_K
     assert torch.equal(pool.state[int(ss[0, 0])], before[int(ss[0, 0])])
+
+
+@pytest.mark.parametrize("conv_width,dtype", [(0, gi.BF16), (4, gi.F32)])
+def test_verify_slots_other_geometries(conv_width, dtype):
+    """No conv front end (snapshot slots get the state only), and fp32
+    inputs at d = 32: the slot path equals verify + rollback bit for bit."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, d_k=32, d_v=32, n_slots=16,
+                            conv_width=conv_width, dtype_in=dtype, dtype_out=dtype, l2norm_qk=conv_width > 0)
+    k = 3
+    inp = gi.verify_inputs(seed=750 + conv_width, geom=g, batch=3, k=k)
+    accepted = [2, 0, 3]
+    pa, snap, oa, pb, ss, ob, nxt = _run_both(g, inp, k, accepted)
+    assert torch.equal(oa, ob)
+    nxt_h = nxt.cpu().numpy()
+    for i, s in enumerate(inp["slots"]):
+        for j in range(k):
+            assert torch.equal(pb.state[int(ss[i, j])], snap[i, j])
+        assert torch.equal(pb.state[int(nxt_h[i])], pa.state[s])
+        o_r, snaps_r, hists_r = orc.verify(g, inp["state"][s], inp["hist"][s], inp["x"][i], inp["a"][i],
+                                           inp["b"][i], inp["conv_w"])
+        assert H.relerr(H.f64(ob[i]), o_r) <= H.tol_for(g)
+    if conv_width:
+        hist_a, hist_b = H.read_hist(g, pa), H.read_hist(g, pb)
+        for i, s in enumerate(inp["slots"]):
+            assert np.array_equal(hist_b[int(nxt_h[i])], hist_a[s])
