@@ -217,3 +217,19 @@ def test_conv_state_step_matches_oracle():
     torch.cuda.synchronize()
     assert np.array_equal(H.read_hist(g, pool), hist.astype(np.float32))
     assert np.array_equal(pool.state.cpu().numpy(), inp["state"])  # state untouched
+
+
+def test_decode_extreme_gates():
+    """Decode with gate inputs at -40 / 40 (exact in bf16): alpha = 1 or e^-40,
+    beta = e^-40 or 1, over several tokens."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=4)
+    inp = gi.decode_inputs(seed=150, geom=g, batch=3, n_tokens=4)
+    rng = np.random.Generator(np.random.PCG64(151))
+    vals = np.array([-40.0, 40.0], np.float32)
+    inp["a"] = vals[rng.integers(0, 2, size=inp["a"].shape)]
+    inp["b"] = vals[rng.integers(0, 2, size=inp["b"].shape)]
+    pool, o_gpu, o_ref, st_ref, _ = _run_decode(g, inp, steps=4)
+    assert np.isfinite(o_gpu).all()
+    assert H.relerr(o_gpu, o_ref) <= H.TOL_BF16
+    for s in inp["slots"]:
+        assert H.relerr(pool.state[s].cpu().numpy(), st_ref[s]) <= H.TOL_BF16

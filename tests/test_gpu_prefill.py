@@ -282,3 +282,23 @@ def test_workload4_varlen_sampled_heads():
     pool, o, err = _prefill(g, inp)
     assert err == 0
     _check(g, inp, pool, o, heads=[5, 30])
+
+
+def test_prefill_extreme_gates():
+    """Gate inputs far out on both sides (a, b in {-40, -8, 0, 8, 40}, exact in
+    bf16): alpha from 1 down to e^-40 and beta from e^-40 up to 1, so whole
+    chunks decay to nothing and others carry the state unchanged."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=3)
+    inp = gi.prefill_inputs(seed=560, geom=g, lengths=[200, 70], init_state=True)
+    rng = np.random.Generator(np.random.PCG64(561))
+    vals = np.array([-40.0, -8.0, 0.0, 8.0, 40.0], np.float32)
+    inp["a"] = vals[rng.integers(0, 5, size=inp["a"].shape)]
+    inp["b"] = vals[rng.integers(0, 5, size=inp["b"].shape)]
+    # one stretch of long memory (alpha = 1, beta = 1) and one of full decay
+    inp["a"][10:80] = -40.0
+    inp["b"][10:80] = 40.0
+    inp["a"][120:140] = 40.0
+    pool, o, err = _prefill(g, inp)
+    assert err == 0
+    assert torch.isfinite(o.float()).all() and torch.isfinite(pool.state).all()
+    _check(g, inp, pool, o)
