@@ -125,11 +125,14 @@ def test_checkpoints_full_geometry_sampled_heads():
     _same_as_plain(g, inp, pool, o)
 
 
-def test_checkpoints_segmented_launches():
-    """96 v-heads: the chain runs as 16-chunk launch segments; a checkpoint
-    falls inside a segment and one on a segment's last chunk (1024 tokens)."""
+@pytest.mark.parametrize("lengths", [[1100, 70], [600, 700]])
+def test_checkpoints_segmented_launches(lengths):
+    """96 v-heads: the chain runs as 16-chunk launch segments, one chain
+    workgroup set per sequence; checkpoints inside a segment, on a segment's
+    last chunk (1024 tokens), and in both sequences of one launch (the second
+    sequence's numbered after the first's)."""
     g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=16, n_v_heads=96, n_slots=2)
-    inp = gi.prefill_inputs(seed=612, geom=g, lengths=[1100, 70], init_state=True, a_mean=-2.0)
+    inp = gi.prefill_inputs(seed=612 + lengths[1], geom=g, lengths=lengths, init_state=True, a_mean=-2.0)
     pool, o, ckpt, err = _run(g, inp, 256)
     assert err == 0
     _check_ckpts(g, inp, 256, ckpt, heads=[0, 13, 95])
