@@ -103,6 +103,10 @@ def parse():
                    help="run only the counter workload: a 1 GiB calibration copy, then two prefills")
     p.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the prefill traffic summary from two rocprofv3 --pmc counter CSVs")
+    p.add_argument("--pmc-probe-decode", action="store_true",
+                   help="run only the decode counter workload: the calibration copy, then four decode calls")
+    p.add_argument("--pmc-summarize-decode", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the decode traffic summary from two rocprofv3 --pmc counter CSVs")
     return p.parse_args()
 
 
@@ -152,6 +156,73 @@ def pmc_probe():
         gdn.prefill_chunked(geom, pool, *args, cw, cu, sl, hi, o, ws)
         torch.cuda.synchronize()
     print("pmc probe done", flush=True)
+
+
+def pmc_probe_decode():
+    """Counter workload for the decode step: the calibration copy, then one
+    4-slot decode on each of 4 slot pools (100 MB of state between them, so
+    each call finds its state cold); the last call is the one summarised."""
+    import torch
+    import gated_deltanet_delta_amd as gdn
+    import gdn_inputs as gi
+    gdn.lib()
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = gi.GEOM_QWEN
+    geom = gdn.Geometry()
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    dinp = gi.workload(2)
+    pools = []
+    for _ in range(4):
+        pl = gdn.SlotPool.zeros(geom)
+        pl.state.normal_(0.0, 0.02)
+        pools.append(pl)
+    x, a, b = (torch.from_numpy(dinp[k][:, 0]).to(bf).to(dev) for k in ("x", "a", "b"))
+    cw = torch.from_numpy(dinp["conv_w"]).to(dev)
+    sl = torch.from_numpy(dinp["slots"]).to(dev)
+    o = torch.empty(4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    torch.cuda.synchronize()
+    for pl in pools:
+        gdn.decode_step(geom, pl, x, a, b, cw, sl, o)
+        torch.cuda.synchronize()
+    print("pmc decode probe done", flush=True)
+
+
+def pmc_summarize_decode(fetch_csv, write_csv):
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = pmc_read(path, counter)
+        calib = max((r for r in rows if "elementwise" in r[1]), key=lambda r: r[2])
+        last = [r for r in rows if "step_kernel" in r[1]][-1]
+        factor = CALIB_BYTES / (calib[2] * 1024.0)
+        out[counter] = (calib[2], factor, last[2] * 1024.0 * factor)
+    lines = ["# Decode step HBM traffic, 4 slots (16 k-heads, 48 v-heads, d = 128, bf16 inputs, fp32 state)", "",
+             "Commands (from /tmp, TMPDIR=/tmp), one counter per run:", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d <dir_f> -o f --output-format csv -- python3 bench.py --pmc-probe-decode",
+             "    rocprofv3 --pmc WRITE_SIZE -d <dir_w> -o w --output-format csv -- python3 bench.py --pmc-probe-decode",
+             "    python3 bench.py --pmc-summarize-decode <dir_f>/f_counter_collection.csv "
+             "<dir_w>/w_counter_collection.csv", "",
+             "Scaled by the same %d-byte calibration copy as the prefill summary; the figures" % CALIB_BYTES,
+             "are the last of four decode calls, each on a slot pool of its own.", "",
+             "| counter | calibration copy (KiB) | scale | decode call (bytes) | algorithmic (bytes) |",
+             "|---|---|---|---|---|"]
+    alg = {"FETCH_SIZE": DECODE_BYTES - DECODE_STATE_BYTES // 2, "WRITE_SIZE": DECODE_STATE_BYTES // 2}
+    for c, (kib, f, v) in out.items():
+        lines.append("| %s | %.0f | %.4f | %.0f | %d |" % (c, kib, f, v, alg[c]))
+    total = out["FETCH_SIZE"][2] + out["WRITE_SIZE"][2]
+    lines += ["", "The algorithmic read is the state (12 582 912 B), the conv history, x, a, b and the",
+              "conv weights; the algorithmic write is the state (o, the ring row and the position are",
+              "counted with the reads' total of %d B)." % DECODE_BYTES, "",
+              "measured_total_bytes: %.0f" % total, "algorithmic_bytes: %d" % DECODE_BYTES, ""]
+    path = os.path.join(ROOT, "profiles", "decode_traffic_4slots.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", path, "measured", int(total), "algorithmic", DECODE_BYTES)
 
 
 def pmc_read(path, counter):
@@ -223,6 +294,9 @@ def main():
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return
+    if args.pmc_summarize_decode:
+        pmc_summarize_decode(*args.pmc_summarize_decode)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the layer's multi-GPU "
                                    "sharding is a design note, not a measured path", "n_gpus": args.gpus}))
@@ -236,6 +310,9 @@ def main():
 
     if args.pmc_probe:
         pmc_probe()
+        return
+    if args.pmc_probe_decode:
+        pmc_probe_decode()
         return
     gdn.lib()
     dev = torch.device("cuda:0")
