@@ -107,16 +107,16 @@ gdn_status check_geometry(const gdn_geometry* g) {
   if (!std::isfinite(g->l2_eps) || g->l2_eps < 0.f)
     return fail(GDN_ERR_GEOMETRY, "l2_eps: %g, required: finite and >= 0", g->l2_eps);
   if (g->conv_width != 0 && g->conv_width != 4)
-    return fail(GDN_ERR_UNSUPPORTED, "conv_width: %d, required in this build: 0 or 4", g->conv_width);
+    return fail(GDN_ERR_UNSUPPORTED, "conv_width: %d, supported by this library: 0 or 4", g->conv_width);
   if (g->d_k != g->d_v)
-    return fail(GDN_ERR_UNSUPPORTED, "d_v: %d, required in this build: equal to d_k = %d", g->d_v, g->d_k);
+    return fail(GDN_ERR_UNSUPPORTED, "d_v: %d, supported by this library: equal to d_k = %d", g->d_v, g->d_k);
   if (g->d_k != 16 && g->d_k != 32 && g->d_k != 64 && g->d_k != 128)
-    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d, required in this build: 16, 32, 64 or 128", g->d_k);
+    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d, supported by this library: 16, 32, 64 or 128", g->d_k);
   if (g->n_v_heads / g->n_k_heads > 8)
-    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads/n_k_heads: %d, required in this build: <= 8",
+    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads/n_k_heads: %d, supported by this library: <= 8",
                 g->n_v_heads / g->n_k_heads);
   if (step_wgs_per_slot(*g) > (1 << 16))
-    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads: %d, required in this build: at most %d workgroups per slot",
+    return fail(GDN_ERR_UNSUPPORTED, "n_v_heads: %d, supported by this library: at most %d workgroups per slot",
                 g->n_v_heads, 1 << 16);
   return ok();
 }
@@ -417,9 +417,9 @@ static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   if (chunk != gdn::kChunk)
-    return fail(GDN_ERR_UNSUPPORTED, "chunk: %d, required in this build: %d", chunk, gdn::kChunk);
+    return fail(GDN_ERR_UNSUPPORTED, "chunk: %d, supported by this library: %d", chunk, gdn::kChunk);
   if (g->dtype_in == GDN_F32 && g->d_k > 64)
-    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d with dtype_in GDN_F32, required for prefill in this build: <= 64",
+    return fail(GDN_ERR_UNSUPPORTED, "d_k: %d with dtype_in GDN_F32, supported by this library for prefill: <= 64",
                 g->d_k);
   if (n_seqs < 1 || n_seqs > g->n_slots)
     return fail(GDN_ERR_RANGE, "n_seqs: %d, required: 1..n_slots = %d", n_seqs, g->n_slots);

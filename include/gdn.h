@@ -91,7 +91,7 @@ typedef enum gdn_status {
   GDN_ERR_NULL = 1,          /* a required pointer is NULL */
   GDN_ERR_ALIGN = 2,         /* a pointer is not 16-byte aligned */
   GDN_ERR_GEOMETRY = 3,      /* inconsistent gdn_geometry */
-  GDN_ERR_UNSUPPORTED = 4,   /* a valid geometry this build has no kernels for */
+  GDN_ERR_UNSUPPORTED = 4,   /* a valid geometry the library has no kernels for */
   GDN_ERR_RANGE = 5,         /* a size argument out of range (batch, k, n_tokens...) */
   GDN_ERR_WORKSPACE = 6,     /* workspace smaller than gdn_prefill_workspace_bytes() */
   GDN_ERR_LAUNCH = 7         /* the HIP runtime refused a launch */
@@ -119,7 +119,7 @@ typedef struct gdn_geometry {
   int32_t n_k_heads;      /* H_k */
   int32_t n_v_heads;      /* H_v, a multiple of H_k */
   int32_t d_k;            /* state columns (ssm_state_size) */
-  int32_t d_v;            /* state rows; this build requires d_v == d_k in {16,32,64,128} */
+  int32_t d_v;            /* state rows; the library requires d_v == d_k in {16,32,64,128} */
   int32_t conv_width;     /* W in {0,2,3,4}; 0 = no conv and no SiLU: x holds q | k | v */
   int32_t conv_channels;  /* C, must equal 2*H_k*d_k + H_v*d_v */
   int32_t conv_ring;      /* R, power of two >= W-1+max_draft (ignored when W = 0) */

@@ -4,7 +4,7 @@ Only the test-suite, the smoke check and the benchmark's CPU-baseline leg
 use this module.  The product path (the HIP library and its binding) never
 imports it, and it imports nothing from the product path.
 
-Sources.  The pages this build follows are cited by title and section:
+Sources.  The pages followed here are cited by title and section:
 
   [Hybrid]  "Hybrid transformers under load: where Gated DeltaNet loses to
             full attention" (braintools.ru).  Section 3 describes the layer in

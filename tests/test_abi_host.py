@@ -149,7 +149,7 @@ def test_prefill_refusals(gdn):
         return L.gdn_prefill_chunked(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), _p(), _p(), cu, _p(), _p(),
                                      n_seqs, n_tokens, chunk, _p(), ws, _p(), None, None)
     assert call(chunk=128) == 4
-    assert "chunk: 128, required in this build: 64" in L.gdn_last_error().decode()
+    assert "chunk: 128, supported by this library: 64" in L.gdn_last_error().decode()
     assert call(ws=need - 1) == 6
     assert f"required: >= {need}" in L.gdn_last_error().decode()
     assert call(n_seqs=9) == 5
