@@ -450,11 +450,12 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     return cc < D ? kh * D + cc : (cc < 2 * D ? Hk * D + kh * D + (cc - D) : 2 * Hk * D + kh * G * D + (cc - 2 * D));
   };
 
-  // gate inputs of the v-head whose gates this wave computes (the last G
-  // waves, one head each), loaded before the conv so they arrive under it;
-  // they stay raw until the gates are computed, so nothing waits for them here
+  // gate inputs of the v-head whose gates this wave computes (the first G
+  // waves, one head each: q|k waves, whose conv items end before the v
+  // items, which also store V), loaded before the conv so they arrive under
+  // it; they stay raw until the gates are computed, so nothing waits for them here
   static_assert(kMaxGroup <= kChunkWaves, "one gate head per wave");
-  const int ghi = kChunkWaves - 1 - wave;
+  const int ghi = wave;
   E a_raw{}, b_raw{};
   if (ghi < G && lane < len) {
     const size_t i = static_cast<size_t>(t0 + lane) * Hv + kh * G + ghi;
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(PrefillArgs A, Pre
     for (int jj = lane + 64; jj < ipw; jj += 64) conv_item(jj);
   }
 
-  // ---- gates: one wave per v-head (the last waves), lane = token, fixed-order inclusive scan ----
+  // ---- gates: one wave per v-head (the first waves), lane = token, fixed-order inclusive scan ----
   if (ghi < G) {
     const int hi = ghi, h = kh * G + hi;
     float g = 0.f, bb = 0.f;
