@@ -26,6 +26,7 @@ POS_ONE = 65536
 POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
+ABI_VERSION = 3  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
 DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
@@ -67,6 +68,7 @@ _SIGS = {
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_version": (ctypes.c_char_p, []),
+    "gdn_abi_version": (ctypes.c_int32, []),
     "gdn_check_geometry": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), ctypes.c_char_p, ctypes.c_size_t]),
     "gdn_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GdnGeometry), _I, _I]),
     "gdn_conv_state_step": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _P, _P, _P]),
@@ -100,6 +102,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.gdn_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.gdn_abi_version()}, this binding needs "
+                               f"{ABI_VERSION}; rebuild it with __graft_entry__.build()")
         _lib = L
     return _lib
 

@@ -174,7 +174,9 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
-const char* gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
+const char* gdn_version(void) { return "gdn-mi355x 0.2 (gfx950)"; }
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len) {
   const gdn_status s = check_geometry(g);

@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3  /* 3: checkpoint prefill, verify into slots, slot commit, GDN_DEV_BAD_K */
 #define GDN_POS_ONE 65536
 #define GDN_POS_STRIDE 32 /* int32 words per slot in conv_pos */
 
@@ -140,6 +140,10 @@ const char* gdn_last_error(void);
 
 /* Library version string (static storage). */
 const char* gdn_version(void);
+
+/* GDN_ABI_VERSION the library was built with; a caller built against another
+ * version of this header must not use it. */
+int32_t gdn_abi_version(void);
 
 /*
  * Validate a geometry without touching the GPU.  Returns GDN_OK, or an error

@@ -221,6 +221,12 @@ def test_conv_step_refusals(gdn):
     assert "conv_width: 0" in L.gdn_last_error().decode()
 
 
+def test_abi_version_matches_the_header(gdn):
+    src = open(HEADER).read()
+    want = int(re.search(r"#define GDN_ABI_VERSION (\d+)", src).group(1))
+    assert gdn.lib().gdn_abi_version() == want == gdn.ABI_VERSION
+
+
 def test_status_strings(gdn):
     L = gdn.lib()
     assert L.gdn_status_string(0) == b"GDN_OK"
