@@ -227,6 +227,24 @@ def test_abi_version_matches_the_header(gdn):
     assert gdn.lib().gdn_abi_version() == want == gdn.ABI_VERSION
 
 
+def test_plain_c_caller(gdn, tmp_path):
+    """The header compiles as C99 and a C program links the library and uses
+    its host-side entry points (no GPU work)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(gdn.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", libdir, "-lgdn",
+                    "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "c abi ok" in r.stdout
+
+
 def test_status_strings(gdn):
     L = gdn.lib()
     assert L.gdn_status_string(0) == b"GDN_OK"
