@@ -167,3 +167,17 @@ def test_resume_from_a_checkpoint_continues_the_request():
     assert torch.equal(pool2.state[slot2], pool1.state[slot1])
     assert np.array_equal(H.read_hist(g, pool2)[slot2], H.read_hist(g, pool1)[slot1])
     assert gdn.checkpoint_count([tail], every) == 1
+
+
+@pytest.mark.parametrize("lengths", [[0, 5], [0, 0]])
+def test_checkpoints_none_due(lengths):
+    """Sequences shorter than a block (and no tokens at all): no checkpoint is
+    written, an empty checkpoint buffer is accepted, and everything else is
+    what the plain prefill writes."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=3)
+    inp = gi.prefill_inputs(seed=620 + sum(lengths), geom=g, lengths=lengths, init_state=True)
+    inp["has_init"] = np.array([0, 1], np.int32)
+    pool, o, ckpt, err = _run(g, inp, 64)
+    assert err == 0
+    assert ckpt.shape[0] == 0
+    _same_as_plain(g, inp, pool, o)
