@@ -5,8 +5,8 @@
 // Every refusal names the argument, the value found and the value required
 // ("Chapter 6: engine startup and memory plan", section 6.2), and no error is
 // swallowed: a launch the runtime refuses is returned as GDN_ERR_LAUNCH with
-// the runtime's code ("Forge", entry of 27 August: the costliest defect of
-// the week was an error the scheduler dropped without a log line).
+// the runtime's code ("Forge", entry of 27 August, on a scheduler error that
+// went unreported).
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>

@@ -8,11 +8,11 @@ Sources.  The pages followed here are cited by title and section:
 
   [Hybrid]  "Hybrid transformers under load: where Gated DeltaNet loses to
             full attention" (braintools.ru).  Section 3 describes the layer in
-            words: on every token the state is partly erased by a gate
-            ("controlled forgetting") and then receives a correction from the
-            new token (the delta rule, "corrective write instead of blind
-            accumulation"); the introduction names the method's paper,
-            Gated DeltaNet, arXiv:2412.06464.  Section 3 also states that the
+            words: each token first decays the state through a learned gate,
+            then overwrites what the state returns for the token's key with
+            the token's value (the delta rule), instead of only adding to it;
+            the introduction names the method's paper, Gated DeltaNet,
+            arXiv:2412.06464.  Section 3 also states that the
             state has a fixed size whatever the context length; section 4.1
             prints the state byte counts; section 9 keeps states in fp32.
             Sections 3, 4.2 and 6.1 motivate state checkpoints at block
@@ -173,7 +173,9 @@ def delta_rule_step(S, q, k, v, g, beta, q_scale=1.0):
 def delta_rule_step_matrix(S, q, k, v, g, beta, q_scale=1.0):
     """The same step with the transition matrix (I - beta k k^T) formed explicitly.
 
-    Used by the tests on small d only, to pin the expanded form above.
+    The rule exactly as it is written, for small d: the pins compare the
+    expanded form above with it, and check both against the transition's
+    closed-form action on k and on the directions orthogonal to k.
     """
     H, dv, dk = S.shape
     out_S = np.empty_like(S, dtype=F64)

@@ -169,20 +169,91 @@ def pin_conv_history(m):
 # --------------------------------------------------------------------------
 
 def pin_expanded_equals_matrix_form(m):
+    """The expanded step (no d_k x d_k matrix) equals the step with the
+    transition matrix (I - beta k k^T) formed explicitly, the rule as written;
+    the transition's own action is pinned by pin_transition_action."""
     rng = _rng(21)
     H, d = 3, 5
     S = rng.normal(size=(H, d, d))
-    q, k = _unit(rng, H, d), _unit(rng, H, d)
+    q, k = rng.normal(size=(H, d)), 1.7 * _unit(rng, H, d)
     v = rng.normal(size=(H, d))
     g = -rng.uniform(0, 2, size=H)
     beta = rng.uniform(0, 1, size=H)
     S1, o1 = m.delta_rule_step(S, q, k, v, g, beta, 0.7)
-    # the rule as printed, with the transition matrix formed explicitly
-    for h in range(H):
-        M = np.eye(d) - beta[h] * np.outer(k[h], k[h])
-        Sref = np.exp(g[h]) * S[h] @ M + beta[h] * np.outer(v[h], k[h])
-        _close(S1[h], Sref, 1e-14, "S_t vs alpha S (I - beta k k^T) + beta v k^T")
-        _close(o1[h], 0.7 * Sref @ q[h], 1e-14, "o_t = q_scale S_t q_t")
+    S2, o2 = m.delta_rule_step_matrix(S, q, k, v, g, beta, 0.7)
+    _close(S1, S2, 1e-14, "expanded vs matrix form: S_t")
+    _close(o1, o2, 1e-14, "expanded vs matrix form: o_t")
+
+
+def pin_transition_action(m):
+    """For a unit key the transition I - beta k k^T scales k by (1 - beta) and
+    leaves every direction orthogonal to k alone, so
+        S_t k = alpha (1 - beta) S_{t-1} k + beta v,   S_t u = alpha S_{t-1} u  (u . k = 0),
+        o_t = q_scale S_t q  (linear in q).
+    Checked on both the expanded and the matrix form of the step."""
+    rng = _rng(35)
+    H, d = 3, 6
+    for step in (m.delta_rule_step, m.delta_rule_step_matrix):
+        S = rng.normal(size=(H, d, d))
+        k = _unit(rng, H, d)
+        q = rng.normal(size=(H, d))
+        v = rng.normal(size=(H, d))
+        g = -rng.uniform(0, 2, size=H)
+        beta = rng.uniform(0, 1, size=H)
+        S1, o1 = step(S, q, k, v, g, beta, 0.3)
+        alpha = np.exp(g)
+        Sk = np.einsum("hij,hj->hi", S, k)
+        _close(np.einsum("hij,hj->hi", S1, k),
+               (alpha * (1 - beta))[:, None] * Sk + beta[:, None] * v, 1e-13,
+               f"{step.__name__}: action on k")
+        u = rng.normal(size=(H, d))
+        u -= (u * k).sum(1, keepdims=True) * k  # orthogonal to k
+        _close(np.einsum("hij,hj->hi", S1, u), alpha[:, None] * np.einsum("hij,hj->hi", S, u), 1e-13,
+               f"{step.__name__}: action orthogonal to k")
+        _, o2 = step(S, 2.0 * q, k, v, g, beta, 0.3)
+        _close(o2, 2.0 * o1, 1e-14, f"{step.__name__}: o linear in q")
+        _close(o1, 0.3 * np.einsum("hij,hj->hi", S1, q), 1e-14, f"{step.__name__}: o from the new state")
+
+
+def pin_no_conv_front_end(m):
+    """Without the conv front end (conv_width = 0, the tiny workload's layout)
+    x holds q | k | v and the layer applies nothing to them: no conv, no SiLU,
+    no norm.  Keys and queries of arbitrary length show any of those:
+      - first token from a zero state: S_1 = beta v k^T, o_1 = beta (k . q) v;
+      - beta = 0: o_t = e^{sum_{s<=t} g_s} S_0 q_t (linear in the raw q);
+      - a whole sequence equals the plain recurrence on the split x."""
+    geom = dataclasses.replace(gi.GEOM_TINY, n_k_heads=2, n_v_heads=4, d_k=5, d_v=3)
+    rng = _rng(36)
+    Hk, Hv, dk, dv = 2, 4, 5, 3
+    T = 7
+    q = 2.5 * rng.normal(size=(T, Hk, dk))
+    k = 0.6 * rng.normal(size=(T, Hk, dk))
+    v = rng.normal(size=(T, Hv, dv))
+    x = np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
+    a = rng.normal(size=(T, Hv))
+    b = rng.normal(size=(T, Hv))
+    w = np.zeros((geom.conv_channels, 0))
+    hist = np.zeros((0, geom.conv_channels))
+    grp = Hv // Hk
+    qh, kh = np.repeat(q, grp, axis=1), np.repeat(k, grp, axis=1)
+    beta = scipy.special.expit(b)
+    g = -np.logaddexp(0.0, a)
+    # first token from zero
+    o, S, _ = m.layer_sequence(geom, x[:1], a[:1], b[:1], w, np.zeros((Hv, dv, dk)), hist)
+    _close(S, beta[0][:, None, None] * v[0][:, :, None] * kh[0][:, None, :], 1e-15, "W=0 first-token state")
+    _close(o[0], (beta[0] * (kh[0] * qh[0]).sum(1))[:, None] * v[0], 1e-14, "W=0 first-token output")
+    # beta = 0 over the sequence
+    S0 = rng.normal(size=(Hv, dv, dk))
+    b0 = np.full_like(b, -1000.0)
+    o, S, _ = m.layer_sequence(geom, x, a, b0, w, S0, hist)
+    G = np.cumsum(g, axis=0)
+    for t in range(T):
+        _close(o[t], np.exp(G[t])[:, None] * np.einsum("hij,hj->hi", S0, qh[t]), 1e-13, f"W=0 beta=0 t={t}")
+    # the whole layer equals the recurrence on the split input
+    o, S, _ = m.layer_sequence(geom, x, a, b, w, S0, hist)
+    o2, S2 = m.recurrence(qh, kh, v, g, beta, S0)
+    _close(o, o2, 1e-14, "W=0 layer vs recurrence: o")
+    _close(S, S2, 1e-14, "W=0 layer vs recurrence: S")
 
 
 def pin_beta_zero(m):

@@ -48,6 +48,11 @@ MUTATIONS = [
      "conv_w, S_full, 0 * hist, heads=heads)"),
     ("checkpoint_position_relative_to_batch", "where.append((s, p1 - t0))",
      "where.append((s, p1))"),
+    ("norm_without_conv", "if geom.l2norm_qk and geom.conv_width > 0:", "if True:"),
+    ("silu_without_conv", "y = np.asarray(window[-1], F64)", "y = silu(np.asarray(window[-1], F64))"),
+    ("matrix_form_no_beta", "M = np.eye(dk) - beta[h] * np.outer(k[h], k[h])",
+     "M = np.eye(dk) - np.outer(k[h], k[h])"),
+    ("matrix_form_transposed", "out_S[h] = np.exp(g[h]) * (S[h] @ M)", "out_S[h] = np.exp(g[h]) * (M @ S[h])"),
     ("state_bytes_fp16", "return 4 * n_slots * geom.n_v_heads", "return 2 * n_slots * geom.n_v_heads"),
 ]
 
