@@ -26,13 +26,14 @@ POS_ONE = 65536
 POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
-ABI_VERSION = 3  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
+ABI_VERSION = 4  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
 DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
 DEV_BAD_SEQLENS = 3
 DEV_WAIT_TIMEOUT = 4
 DEV_BAD_K = 5
+DEV_INCOMPLETE = 6
 
 
 class GdnGeometry(ctypes.Structure):
@@ -309,6 +310,32 @@ def commit_slots(geom: Geometry, slot, snap_slot, accepted, next_slot, dev_err=N
                                   k, _ptr(next_slot), _ptr(dev_err), _stream(stream)))
 
 
+_err_words = {}
+
+
+def _default_err(device) -> torch.Tensor:
+    """The binding's own device error word of a device (prefill calls without
+    a dev_err of their own report into it; read it with device_error())."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    w = _err_words.get(idx)
+    if w is None:
+        w = torch.zeros(1, dtype=torch.int32, device=torch.device("cuda", idx))
+        _err_words[idx] = w
+    return w
+
+
+def device_error(device="cuda", clear: bool = True) -> int:
+    """First device error code the prefill calls without a dev_err of their
+    own reported on this device since the last clear (synchronises)."""
+    w = _default_err(device)
+    v = int(w.item())
+    if clear and v:
+        w.zero_()
+    return v
+
+
 def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_seqs: int) -> int:
     g = geom.c_struct()
     return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(g), n_tokens, n_seqs))
@@ -328,6 +355,8 @@ def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens,
     writes the state after every ckpt_every tokens of each sequence into ckpt,
     an fp32 device tensor [n][H_v][d_v][d_k] with n >= n_tokens // ckpt_every
     (see ``checkpoint_count`` for the number a partition produces).
+    Without a dev_err of the caller's, device errors go to the binding's own
+    word for the device (``device_error``).
     """
     N = x.shape[0]
     S = slot.shape[0]
@@ -342,6 +371,8 @@ def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens,
     _need(has_init, "has_init", (S,), torch.int32)
     _need(o, "o", (N, Hv, dv), geom.dtype)
     _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    if dev_err is None:  # a stalled hand-off or unscheduled work is never silent
+        dev_err = _default_err(x.device)
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace: must be a contiguous device tensor")
     g = geom.c_struct()
@@ -377,4 +408,5 @@ __all__ = [
     "rollback", "verify_k_slots", "commit_slots", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
     "checkpoint_count", "POS_ONE", "CHUNK",
     "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS", "DEV_WAIT_TIMEOUT", "DEV_BAD_K",
+    "DEV_INCOMPLETE", "device_error",
 ]

@@ -189,8 +189,7 @@ gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len) 
 
 size_t gdn_prefill_workspace_bytes(const gdn_geometry* g, int32_t n_tokens, int32_t n_seqs) {
   if (check_geometry(g) != GDN_OK || n_tokens < 0 || n_seqs < 1) return 0;
-  const int maxc = gdn::prefill_max_chunks(n_tokens, n_seqs);
-  return gdn::prefill_layout(g->n_k_heads, g->n_v_heads, g->d_k, g->dtype_in == GDN_BF16, maxc, n_seqs).total;
+  return gdn::prefill_layout(g->n_k_heads, g->n_v_heads, g->d_k, g->dtype_in == GDN_BF16, n_tokens, n_seqs).total;
 }
 
 gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t* conv_pos, const void* x,
@@ -400,8 +399,8 @@ gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* 
                                     int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                     size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
                                     size_t ckpt_bytes, int32_t* dev_err, void* stream) {
-  if (ckpt_every <= 0 || ckpt_every % gdn::kChunk != 0)
-    return fail(GDN_ERR_RANGE, "ckpt_every: %d, required: a positive multiple of %d", ckpt_every, gdn::kChunk);
+  if (ckpt_every <= 0)
+    return fail(GDN_ERR_RANGE, "ckpt_every: %d, required: > 0", ckpt_every);
   return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
                       n_tokens, chunk, workspace, workspace_bytes, o, ckpt_every, ckpt, ckpt_bytes, dev_err,
                       stream, "gdn_prefill_chunked_ckpt");

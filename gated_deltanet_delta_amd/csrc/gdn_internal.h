@@ -50,22 +50,31 @@ struct PrefillArgs {
   int32_t Hk, Hv, D, C, W, R, n_slots;
   uint32_t flags;
   float q_scale, l2_eps;
-  int32_t seg_lo, seg_hi;  // chunk-table range of one launch segment (set by the launcher)
-  int32_t persistent;      // 1: one chain launch over whole sequences, waiting on per-chunk ready flags
   float* ckpt;             // state checkpoints [n][Hv][D][D], or null
-  int32_t ckpt_every;      // tokens between checkpoints (a multiple of kChunk), 0: none
+  int32_t ckpt_every;      // tokens between checkpoints, 0: none
+  // set by the launcher for each launch of the fused kernel
+  int32_t kh_lo, kh_hi;    // k-heads [kh_lo, kh_hi) of this launch
+  int32_t seg;             // launch index (selects its counters)
+  int32_t last_seg;        // 1 on the launch that writes the ring positions
 };
 
-// Byte offsets and block sizes of the prefill workspace.
-//   kq:   per (chunk, k-head) block of packed Q operand tiles (kq_bytes each)
-//   head: per (chunk, v-head) block of packed -W, decayed K^T, P, U', the gate factors and V (head_bytes each)
-//   ready: per (chunk, k-head) flag, set once the chunk kernel has published that block
+// Byte offsets of the prefill workspace.  Its size does not depend on the
+// number of tokens: chunks pass from producer to chain workgroups through a
+// ring of ring_slots chunk slots.
+//   ring:     [ring_slots][Hk] blocks of item_bytes (packed operands of one (chunk, k-head))
+//   hdr:      total chunk count and the abort word
+//   seq_tab:  per-sequence table (int32 x 8 each)
+//   ready:    per (ring slot, k-head) publish flag = chunk + 1, one 128-byte line each
+//   consumed: per v-head, chunks staged by its chain workgroup, one line each
+//   ctr:      per launch: role and item tickets per XCD, the exit word
 struct PrefillLayout {
-  size_t kq, head, chunk_tab, seq_tab, ready, total;
-  size_t kq_bytes, head_bytes;
+  size_t ring, hdr, seq_tab, ready, consumed, ctr, total;
+  size_t item_bytes;
+  int32_t ring_slots;
 };
-PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int max_chunks, int n_seqs);
+PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int n_tokens, int n_seqs);
 int prefill_max_chunks(int n_tokens, int n_seqs);
+int prefill_launches(int Hk, int Hv);
 constexpr int kChunk = 64;
 
 // Launchers: return 0 on success, else the hipError_t value.

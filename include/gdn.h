@@ -82,7 +82,8 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3  /* 3: checkpoint prefill, verify into slots, slot commit, GDN_DEV_BAD_K */
+#define GDN_ABI_VERSION 4  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
+                              checkpoints at any block size, GDN_DEV_INCOMPLETE */
 #define GDN_POS_ONE 65536
 #define GDN_POS_STRIDE 32 /* int32 words per slot in conv_pos */
 
@@ -102,8 +103,9 @@ typedef enum gdn_status {
 #define GDN_DEV_BAD_SLOT 1       /* slot id outside [0, n_slots) */
 #define GDN_DEV_BAD_ACCEPTED 2   /* accepted length outside [0, k] */
 #define GDN_DEV_BAD_SEQLENS 3    /* cu_seqlens[0] != 0, decreasing, or last != n_tokens */
-#define GDN_DEV_WAIT_TIMEOUT 4   /* prefill: a chunk's operands were not published in time; outputs invalid */
+#define GDN_DEV_WAIT_TIMEOUT 4   /* prefill: a hand-off between its workgroups stalled (bounded wait); outputs invalid */
 #define GDN_DEV_BAD_K 5          /* a row's draft count outside [1, k] */
+#define GDN_DEV_INCOMPLETE 6     /* prefill: part of the work was never picked up by a workgroup; outputs invalid */
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
@@ -156,18 +158,14 @@ gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len);
 /*
  * Workspace bytes gdn_prefill_chunked needs for n_tokens tokens in n_seqs
  * sequences with 64-token chunks (0 when the geometry is invalid).  Host only.
+ * The size is bounded independently of n_tokens: chunks pass between the
+ * prefill's workgroups through a ring of at most 16 chunk slots (fewer when
+ * the call has fewer chunks), plus a table of n_seqs entries and flags.
+ * ("Chapter 6: engine startup and memory plan", section 6.10: the memory
+ * of the token path is planned up front and bounded.)
  */
 size_t gdn_prefill_workspace_bytes(const gdn_geometry* g, int32_t n_tokens, int32_t n_seqs);
 
-/*
- * One token of the conv ring alone: for each batch row i with slot s = slot[i],
- *   y[i][c] = SiLU(sum_j conv_w[c][j] * window_j[c])   (window: W-1 ring rows, then x[i])
- * then x[i] is appended to the slot's ring and conv_pos[s] advances by one token.
- * (Conv width 4 and channel count: "Chapter 6", section 6.2; the conv part of
- * the per-layer state: "Hybrid transformers under load", section 4.1.)
- *   x [batch][C] dtype_in, y [batch][C] dtype_out, slot [batch] int32 (device).
- * Requires W > 0.  1 <= batch <= n_slots.
- */
 gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t* conv_pos,
                                const void* x, const float* conv_w, const int32_t* slot,
                                int32_t batch, void* y, int32_t* dev_err, void* stream);
@@ -199,13 +197,16 @@ gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_stat
  *   slot, has_init [n_seqs] int32 (device).
  *   workspace: device, >= gdn_prefill_workspace_bytes(g, n_tokens, n_seqs).
  *   1 <= n_seqs <= n_slots, 0 <= n_tokens.
- * The call enqueues work on `stream` and on a library-owned stream of the
- * current device; before it returns, `stream` is made to wait for all of it,
- * so later work on `stream` sees the results.  Calls that share a workspace
- * must be ordered on one stream.  *dev_err receives GDN_DEV_WAIT_TIMEOUT if
- * the internal producer/consumer hand-off ever stalls (the outputs are then
- * not valid).  The two kernels of one call must run at the same time, so the
- * call is made directly on a stream, not captured into a graph.
+ * Both kernels of the call (a planning kernel, then one launch that holds
+ * the chunk-parallel and the sequential parts as cooperating workgroups) are
+ * enqueued on `stream` alone; the call creates no stream or event and keeps
+ * no state between calls, so it may be captured into a graph.  Calls that
+ * share a workspace must be ordered on one stream.  *dev_err receives
+ * GDN_DEV_WAIT_TIMEOUT if a hand-off between the launch's workgroups ever
+ * stalls past its bounded wait, or GDN_DEV_INCOMPLETE if part of the work was
+ * never taken up (the outputs are then not valid); the launch always ends.
+ * (The chunked form: the rule of "Hybrid transformers under load", section
+ * 3, reorganised over 64-token chunks; same results up to rounding.)
  */
 gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_state,
                                int32_t* conv_pos, const void* x, const void* a, const void* b,
@@ -219,20 +220,20 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
  * ("Hybrid transformers under load", section 3: reusing a shared prefix needs
  * a saved copy of the state where the prefix ends, since the live state goes
  * on to absorb the rest of the request; section 4.2: such snapshots are taken
- * at every cache-block boundary; section 6.1 measures their cost).
- * Everything gdn_prefill_chunked computes and writes is computed and written
- * the same way, bit for bit; in addition, for each sequence s and each
- * p = ckpt_every, 2 ckpt_every, ... <= n_s, the state after the first p tokens
- * of s (counted within this call) is written to
+ * at every cache-block boundary, 528 tokens there; section 6.1 measures their
+ * cost).  Everything gdn_prefill_chunked computes and writes is computed and
+ * written the same way, bit for bit; in addition, for each sequence s and
+ * each p = ckpt_every, 2 ckpt_every, ... <= n_s, the state after the first p
+ * tokens of s (counted within this call) is written to
  *   ckpt fp32 [n_ckpt][H_v][d_v][d_k],
  * numbered sequence by sequence in token order: sequence s's checkpoints start
  * at index sum over s' < s of floor(n_s' / ckpt_every).  A sequence whose
  * length is a multiple of ckpt_every ends on a checkpoint equal to its final
- * state.  The conv history at checkpoint p is not written: with
- * ckpt_every >= 64 > W-1 it is the input rows x[cu_seqlens[s] + p - W + 1 ..
- * cu_seqlens[s] + p - 1], which the caller holds.  Entries past the last
- * checkpoint are not touched.
- *   ckpt_every: a positive multiple of `chunk` (checkpoints fall on chunk ends).
+ * state.  The conv history at checkpoint p is not written: it is the input
+ * rows x[cu_seqlens[s] + p - W + 1 .. cu_seqlens[s] + p - 1] (for p >= W-1;
+ * earlier rows come from the sequence's initial history), which the caller
+ * holds.  Entries past the last checkpoint are not touched.
+ *   ckpt_every: any positive number of tokens (a block may end inside a chunk).
  *   ckpt: device, 16-byte aligned, ckpt_bytes >= floor(n_tokens / ckpt_every)
  *   * H_v * d_v * d_k * 4 (no partition of n_tokens has more checkpoints);
  *   NULL only when that bound is 0.

@@ -104,14 +104,29 @@ def test_checkpoints_varlen_bf16(every):
         assert torch.equal(ckpt[i], pool.state[int(inp["slots"][2])])
 
 
+@pytest.mark.parametrize("every", [528, 100, 40, 7])
+def test_checkpoints_inside_chunks_bf16(every):
+    """Blocks that end inside a chunk ([Hybrid] section 4.2's 528-token block,
+    and blocks shorter than a chunk, several per chunk): lengths 1100, 0, 530
+    and 64 with and without initial state."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=5)
+    inp = gi.prefill_inputs(seed=620 + every, geom=g, lengths=[1100, 0, 530, 64], a_mean=-2.0)
+    inp["has_init"] = np.array([1, 0, 0, 1], np.int32)
+    pool, o, ckpt, err = _run(g, inp, every)
+    assert err == 0
+    _check_ckpts(g, inp, every, ckpt)
+    _same_as_plain(g, inp, pool, o)
+
+
 def test_checkpoints_fp32():
     g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=1, n_v_heads=3, d_k=32, d_v=32, n_slots=4,
                             dtype_in=gi.F32, dtype_out=gi.F32)
     inp = gi.prefill_inputs(seed=610, geom=g, lengths=[70, 257, 128], init_state=True)
-    pool, o, ckpt, err = _run(g, inp, 64)
-    assert err == 0
-    _check_ckpts(g, inp, 64, ckpt)
-    _same_as_plain(g, inp, pool, o)
+    for every in (64, 45):
+        pool, o, ckpt, err = _run(g, inp, every)
+        assert err == 0
+        _check_ckpts(g, inp, every, ckpt)
+        _same_as_plain(g, inp, pool, o)
 
 
 def test_checkpoints_full_geometry_sampled_heads():
