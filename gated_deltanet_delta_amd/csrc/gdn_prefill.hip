@@ -126,14 +126,17 @@ struct Geo {
   static constexpr int KA = 4 * KSD;           // K as A (rows token, k = d): 4 x KSD
   static constexpr int KT = 8 * KSD;           // K^T as A (rows d, k = token): NT x KSC
   static constexpr int HEAD0 = 8 * KSD + NT * KSC;
-  // then per v-head of the group: T diag(beta) and P as A (NTRI tiles each), gates (1 tile)
-  static constexpr int HT = 0, HP = NTRI, HG = 2 * NTRI, HEAD_TILES = 2 * NTRI + 1;
+  // then per v-head of the group: T diag(beta) and P as A (NTRI tiles each),
+  // gates (1 tile), and V in accumulator layout (tile (d_v / 16, token / 16),
+  // lane (token % 16 / 4) * 16 + d_v % 16, element token % 4; NV tiles of 1 KB)
+  static constexpr int NV = NT * 4 * P::VC_BYTES / kTileBytes;
+  static constexpr int HT = 0, HP = NTRI, HG = 2 * NTRI, HV = 2 * NTRI + 1, HEAD_TILES = HV + NV;
   // gate tile: e^G [64], e^{G_last - G} [64], G [64], e^{G_last} (64 copies)
   static constexpr int G_EG = 0, G_D = 64, G_G = 128, G_EGL = 192;
-  // A chain stage in LDS: the item's shared tiles, one head's tiles, then V
+  // A chain stage in LDS: the item's shared tiles, then one head's tiles
   static constexpr int STAGE_TILES = HEAD0 + HEAD_TILES;
-  static constexpr size_t V_OFF = static_cast<size_t>(STAGE_TILES) * kTileBytes;
-  static constexpr size_t STAGE_BYTES = V_OFF + static_cast<size_t>(NT) * 4 * P::VC_BYTES;
+  static constexpr size_t V_OFF = static_cast<size_t>(HEAD0 + HV) * kTileBytes;
+  static constexpr size_t STAGE_BYTES = static_cast<size_t>(STAGE_TILES) * kTileBytes;
   static constexpr int NBUF = 2 * STAGE_BYTES <= kLdsStageMax ? 2 : 1;
   // chain compute waves: CT 16-row tiles of d_v each
   static constexpr int CT = NT >= 2 ? 2 : 1;
@@ -315,6 +318,13 @@ struct Chain<true> {
   __device__ static f32x4_t step(uint4 a, const Bop& b, f32x4_t c) {
     return mfma32(__builtin_bit_cast(bf16x8_t, a), b, c);
   }
+  // The transposed product: a lane supplies A[row l%16][k-set] and B[k-set][col
+  // l%16] in the same register positions, so B-operand registers of X (k, n)
+  // are the A operand of X^T (rows n, k) and a packed A tile of Y (rows m, k)
+  // is the B operand of Y^T (k, cols m).
+  __device__ static f32x4_t step_t(const Bop& a, uint4 b, f32x4_t c) {
+    return mfma32(a, __builtin_bit_cast(bf16x8_t, b), c);
+  }
 };
 
 template <>
@@ -326,6 +336,12 @@ struct Chain<false> {
     c = mfma4(__uint_as_float(a.y), b[1], c);
     c = mfma4(__uint_as_float(a.z), b[2], c);
     return mfma4(__uint_as_float(a.w), b[3], c);
+  }
+  __device__ static f32x4_t step_t(const Bop& a, uint4 b, f32x4_t c) {
+    c = mfma4(a[0], __uint_as_float(b.x), c);
+    c = mfma4(a[1], __uint_as_float(b.y), c);
+    c = mfma4(a[2], __uint_as_float(b.z), c);
+    return mfma4(a[3], __uint_as_float(b.w), c);
   }
 };
 
@@ -438,26 +454,38 @@ struct ChunkPos {
   bool init;
 };
 
-template <bool BF16, int KW>
-__device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp,
-                                             float (&y)[2][16]) {
-  using E = typename Pk<BF16>::E;
+template <bool BF16>
+struct Rows {
   using RawT = typename std::conditional<BF16, uint32_t, uint2>::type;
+  RawT r[19];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_rows(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp, Rows<BF16>& raw) {
+  using E = typename Pk<BF16>::E;
+  using RawT = typename Rows<BF16>::RawT;
   const E* x = static_cast<const E*>(A.x);
   const int C = A.C;
-  RawT raw[19];
   const int tfirst = cp.t0 + tq - 3;
   if (tfirst >= cp.seq_start && tq + 16 <= cp.len) {
     const E* xr = x + static_cast<size_t>(tfirst) * C + c0;
 #pragma unroll
-    for (int i = 0; i < 19; ++i) raw[i] = *reinterpret_cast<const RawT*>(xr + static_cast<size_t>(i) * C);
+    for (int i = 0; i < 19; ++i) raw.r[i] = *reinterpret_cast<const RawT*>(xr + static_cast<size_t>(i) * C);
   } else {
 #pragma unroll
     for (int i = 0; i < 19; ++i) {
       const int t = min(max(tfirst + i, cp.seq_start), cp.t0 + cp.len - 1);
-      raw[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
+      raw.r[i] = *reinterpret_cast<const RawT*>(x + static_cast<size_t>(t) * C + c0);
     }
   }
+}
+
+template <bool BF16, int KW>
+__device__ __forceinline__ void conv_rows(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp,
+                                          const Rows<BF16>& raw, float (&y)[2][16]) {
+  using RawT = typename Rows<BF16>::RawT;
+  const int C = A.C;
+  const int tfirst = cp.t0 + tq - 3;
   auto elem = [&](const RawT& r, int v) -> float {
     if constexpr (BF16) return __uint_as_float(v == 0 ? (r << 16) : (r & 0xffff0000u));
     else return __uint_as_float(v == 0 ? r.x : r.y);
@@ -478,7 +506,7 @@ __device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int t
   for (int i = 0; i < 3; ++i) {
     const int t = tfirst + i;
 #pragma unroll
-    for (int v = 0; v < 2; ++v) hist[v][i] = elem(raw[i], v);
+    for (int v = 0; v < 2; ++v) hist[v][i] = elem(raw.r[i], v);
     if (KW == 4 && t < cp.seq_start) {
       if (cp.init) {
         const float* rr = A.conv_state + (static_cast<size_t>(cp.slot) * A.R +
@@ -495,7 +523,7 @@ __device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int t
   for (int r = 0; r < 16; ++r) {
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const float xin = elem(raw[3 + r], v);
+      const float xin = elem(raw.r[3 + r], v);
       float yy;
       if constexpr (KW == 4) {
         float acc = w[v][0] * hist[v][0];
@@ -510,6 +538,14 @@ __device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int t
       y[v][r] = tq + r < cp.len ? yy : 0.f;
     }
   }
+}
+
+template <bool BF16, int KW>
+__device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp,
+                                             float (&y)[2][16]) {
+  Rows<BF16> raw;
+  load_rows<BF16>(A, c0, tq, cp, raw);
+  conv_rows<BF16, KW>(A, c0, tq, cp, raw, y);
 }
 
 __device__ __forceinline__ ChunkPos chunk_pos(const int32_t* se, int ci) {
@@ -597,12 +633,15 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   auto htile = [&](int hi, int t) { return rtile(Gm::HEAD0 + hi * Gm::HEAD_TILES + t); };
 
   // The ring slot is free once every chain workgroup of this k-head has staged
-  // the chunk it held (RS chunks earlier).  One thread waits; nothing is
-  // written to the slot before the barrier after the gates.
-  if (tid == 0 && chunk >= RS) {
-    const int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
-    for (int hh = 0; hh < G; ++hh)
-      if (!wait_at_least(consumed + (kh * G + hh) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err)) break;
+  // the chunk it held (RS chunks earlier).  One thread waits; the barrier
+  // keeps every wave's stores to the slot behind that wait.
+  if (chunk >= RS) {
+    if (tid == 0) {
+      const int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
+      for (int hh = 0; hh < G; ++hh)
+        if (!wait_at_least(consumed + (kh * G + hh) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err)) break;
+    }
+    lds_barrier();
   }
 
   // gate inputs of the v-head whose gates this wave computes (the first G
@@ -616,17 +655,41 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     b_raw = static_cast<const E*>(A.b)[i];
   }
 
-  // ---- conv + SiLU of q | k: item = (2 channels, 16 tokens) ----
+  // ---- conv + SiLU: item = (2 channels, 16 tokens); the q | k items first
+  // (outputs to LDS), then the v items of the group's heads (V straight to the
+  // ring in accumulator layout).  Each round of kThreads items is all of one
+  // kind, so no wave runs both paths in one round. ----
   {
-    constexpr int NV = D;                 // channel pairs over q | k (2 D channels)
-    for (int item = tid; item < 4 * NV; item += kThreads) {
-      const int q = item / NV, cc0 = 2 * (item % NV);
-      const int c0 = cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
+    constexpr int NQK = 4 * D;             // 2 D channels / 2 per item x 4 quarters
+    const int n_items = NQK + 2 * G * D;   // + G D v channels / 2 x 4 quarters
+    for (int item = tid; item < n_items; item += kThreads) {
       float y[2][16];
-      conv_quarter<BF16, KW>(A, c0, 16 * q, cp, y);
+      if (item < NQK) {
+        const int q = item / D, cc0 = 2 * (item % D);
+        const int c0 = cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
+        conv_quarter<BF16, KW>(A, c0, 16 * q, cp, y);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        *reinterpret_cast<float2*>(qk + (16 * q + r) * QK_LD + cc0) = make_float2(y[0][r], y[1][r]);
+        for (int r = 0; r < 16; ++r)
+          *reinterpret_cast<float2*>(qk + (16 * q + r) * QK_LD + cc0) = make_float2(y[0][r], y[1][r]);
+      } else {
+        const int i2 = item - NQK;
+        const int q = i2 / (G * D / 2), vc = 2 * (i2 % (G * D / 2));   // v channel within the group
+        const int hi = vc / D, dv0 = vc % D;
+        conv_quarter<BF16, KW>(A, 2 * Hk * D + kh * G * D + vc, 16 * q, cp, y);
+        E* vb = reinterpret_cast<E*>(htile(hi, Gm::HV) - 16 * lane);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          E* dst = vb + (((dv0 >> 4) * 4 + q) * 64 + g4 * 16 + (dv0 & 15)) * 4;
+          if constexpr (BF16) {
+            *reinterpret_cast<uint4*>(dst) =
+                make_uint4(pack2_bf16(y[0][4 * g4], y[0][4 * g4 + 1]), pack2_bf16(y[0][4 * g4 + 2], y[0][4 * g4 + 3]),
+                           pack2_bf16(y[1][4 * g4], y[1][4 * g4 + 1]), pack2_bf16(y[1][4 * g4 + 2], y[1][4 * g4 + 3]));
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[0][4 * g4], y[0][4 * g4 + 1], y[0][4 * g4 + 2], y[0][4 * g4 + 3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(y[1][4 * g4], y[1][4 * g4 + 1], y[1][4 * g4 + 2], y[1][4 * g4 + 3]);
+          }
+        }
+      }
     }
   }
 
@@ -871,11 +934,9 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
 // Waves 0 .. NWC-1 compute: wave w holds the 16-row tiles CT w .. CT w + CT-1
 // of d_v, i.e. columns of S^T, as NT accumulator tiles each.  Waves NWC .. 7
 // are helpers: for chunk c+1 while the compute waves work on chunk c, they
-// compute V (conv + SiLU of the v-head's channels, straight from x) into LDS
-// in accumulator layout, wait for the producer's flag and copy the item's
-// operand tiles (the k-head's Q, K, K^T; this v-head's T diag(beta), P and
-// gates) from the L2 into LDS.  One workgroup barrier per chunk swaps the two
-// LDS buffers (two barriers when the geometry leaves room for one buffer).
+// wait for the producer's flag and copy the item's operand tiles from the L2
+// into LDS.  One workgroup barrier per chunk swaps the two LDS buffers (two
+// barriers when the geometry leaves room for one buffer).
 template <int D, bool BF16, int KW, bool CKPT>
 __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int kh, int h) {
   using P = Pk<BF16>;
@@ -901,56 +962,35 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     const int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
     int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
     const char* ringb = static_cast<const char*>(A.workspace) + Lay.ring;
+    // The helper waves walk the same chunks as the compute waves (every valid
+    // sequence's chunks in order): wait for the producer's flag, copy the
+    // item's tiles (the k-head's Q, K, K^T; this v-head's T diag(beta), P,
+    // gates and V) from the L2 into the LDS buffer, and take the barrier.
     constexpr int NCP = (Gm::STAGE_TILES + NHW - 1) / NHW;  // tiles copied per helper wave
-    int c = 0;
-    for (int s = 0; s < S; ++s) {
-      const int32_t* se = stab + 8 * s;
-      if (!(se[SQ_FLAGS] & SQF_VALID)) continue;
-      const int nc = se[SQ_NCHUNK];
-      for (int ci = 0; ci < nc; ++ci, ++c) {
-        char* b = buf(c);
-        const ChunkPos cp = chunk_pos(se, ci);
-        // V = conv + SiLU of the v channels, accumulator layout: tile
-        // (dv / 16, quarter q), lane (token % 16 / 4) * 16 + dv % 16, element token % 4
-        E* vb = reinterpret_cast<E*>(b + Gm::V_OFF);
-        for (int item = hw * 64 + lane; item < 2 * D; item += NHW * 64) {
-          const int q = item / (D / 2), dv0 = 2 * (item % (D / 2));
-          float y[2][16];
-          conv_quarter<BF16, KW>(A, 2 * Hk * D + h * D + dv0, 16 * q, cp, y);
+    int nchunks = 0;
+    for (int s = 0; s < S; ++s)
+      if (stab[8 * s + SQ_FLAGS] & SQF_VALID) nchunks += stab[8 * s + SQ_NCHUNK];
+    for (int c = 0; c < nchunks; ++c) {
+      char* b = buf(c);
+      wait_at_least(ready + ((c % RS) * Hk + kh) * kLine, c + 1, hdr + HDR_ABORT, A.dev_err);
+      const char* rb = ringb + (static_cast<size_t>(c % RS) * Hk + kh) * Lay.item_bytes;
+      uint4 rv[NCP];
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            E* dst = vb + (((dv0 >> 4) * 4 + q) * 64 + g4 * 16 + (dv0 & 15)) * 4;
-            if constexpr (BF16) {
-              *reinterpret_cast<uint4*>(dst) =
-                  make_uint4(pack2_bf16(y[0][4 * g4], y[0][4 * g4 + 1]), pack2_bf16(y[0][4 * g4 + 2], y[0][4 * g4 + 3]),
-                             pack2_bf16(y[1][4 * g4], y[1][4 * g4 + 1]), pack2_bf16(y[1][4 * g4 + 2], y[1][4 * g4 + 3]));
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(y[0][4 * g4], y[0][4 * g4 + 1], y[0][4 * g4 + 2], y[0][4 * g4 + 3]);
-              *reinterpret_cast<float4*>(dst + 4) = make_float4(y[1][4 * g4], y[1][4 * g4 + 1], y[1][4 * g4 + 2], y[1][4 * g4 + 3]);
-            }
-          }
-        }
-        // the item's operand tiles, once the producer has published them
-        wait_at_least(ready + ((c % RS) * Hk + kh) * kLine, c + 1, hdr + HDR_ABORT, A.dev_err);
-        const char* rb = ringb + (static_cast<size_t>(c % RS) * Hk + kh) * Lay.item_bytes;
-        uint4 rv[NCP];
-#pragma unroll
-        for (int j = 0; j < NCP; ++j) {
-          const int t = hw + j * NHW;
-          const int src = t < Gm::HEAD0 ? t : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0);
-          rv[j] = t < Gm::STAGE_TILES ? load_l2(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane))
-                                      : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < NCP; ++j) {
-          const int t = hw + j * NHW;
-          if (t < Gm::STAGE_TILES) *reinterpret_cast<uint4*>(b + static_cast<size_t>(t) * kTileBytes + 16 * lane) = rv[j];
-        }
-        lds_barrier();  // chunk c staged
-        if (hw == 0 && lane == 0)
-          __hip_atomic_store(consumed + h * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (NBUF == 1) lds_barrier();  // the compute waves are done with the buffer
+      for (int j = 0; j < NCP; ++j) {
+        const int t = hw + j * NHW;
+        const int src = t < Gm::HEAD0 ? t : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0);
+        rv[j] = t < Gm::STAGE_TILES ? load_l2(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane))
+                                    : make_uint4(0, 0, 0, 0);
       }
+#pragma unroll
+      for (int j = 0; j < NCP; ++j) {
+        const int t = hw + j * NHW;
+        if (t < Gm::STAGE_TILES) *reinterpret_cast<uint4*>(b + static_cast<size_t>(t) * kTileBytes + 16 * lane) = rv[j];
+      }
+      lds_barrier();  // chunk c staged
+      if (hw == 0 && lane == 0)
+        __hip_atomic_store(consumed + h * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (NBUF == 1) lds_barrier();  // the compute waves are done with the buffer
     }
     return;
   }
@@ -1006,75 +1046,126 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       // The step runs in stages separated by scheduling barriers, in the order
       // that keeps the fewest values live: Y = K S^T -> Z = V - diag(e^G) Y as
       // B operands; O = Q S^T; U = T diag(beta) Z -> U as B operands (plain
-      // and decayed); O += P U; checkpoints; state update.
+      // and decayed); O += P U; checkpoints; state update.  Inside a product
+      // the operand tiles of contraction step ks+1 are read from LDS while
+      // the MFMAs of step ks run, and every tile read feeds all CT tiles.
       auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-      auto bS_of = [&](int ct, int ks) {
-        const int i0 = ks * TPS;
-        return Ch::bop(st[ct][i0], (TPS == 2 && i0 + 1 < NT) ? st[ct][(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
-      };
+      // S^T as B operands (and, read the other way, S as A operands), built
+      // once for both products of the state
+      Bop bS[CT][KSD];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int i0 = ks * TPS;
+          bS[ct][ks] = Ch::bop(st[ct][i0], (TPS == 2 && i0 + 1 < NT) ? st[ct][(i0 + 1) % NT] : f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
       auto gvec = [&](int off, int mt) {
         const float4 v = *reinterpret_cast<const float4*>(gt + off + 16 * mt + 4 * g);
         return f32x4_t{v.x, v.y, v.z, v.w};
       };
+      // acc[ct][mt] += A(mt, ks) S^T(ks) over ks (TR: the transposed product,
+      // acc[ct][mt] += S(ks) A(mt, ks)^T, rows d_v and columns token): the
+      // A tiles of one ks read ahead
+      auto times_S = [&](const uint4* arr, f32x4_t (&acc)[CT][4], auto tr) {
+        constexpr bool TR = decltype(tr)::value;
+        uint4 cur[4], nxt[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) cur[mt] = tile(arr, mt * KSD);
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          if (ks + 1 < KSD) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) nxt[mt] = tile(arr, mt * KSD + ks + 1);
+          }
+          fence();
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              acc[ct][mt] = TR ? Ch::step_t(bS[ct][ks], cur[mt], acc[ct][mt]) : Ch::step(cur[mt], bS[ct][ks], acc[ct][mt]);
+          fence();
+          if (ks + 1 < KSD) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) cur[mt] = nxt[mt];
+          }
+        }
+      };
       // stage 1: Y = K S^T, then Z = V - diag(e^G) Y as B operands of the T product
       Bop bZ[CT][KSC];
+      {
+        // V and e^G are read first, so they arrive under the products
+        using VRaw = typename std::conditional<BF16, uint2, float4>::type;
+        VRaw vr[CT][4];
+        f32x4_t egv[4];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        f32x4_t Y[4];
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) Y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < 4; ++mt)
+            vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((dvt0 + ct) * 4 + mt) * 64 + lane) * 4);
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          const Bop b = bS_of(ct, ks);
+        for (int mt = 0; mt < 4; ++mt) egv[mt] = gvec(Gm::G_EG, mt);
+        f32x4_t Y[CT][4];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) Y[mt] = Ch::step(tile(ka, mt * KSD + ks), b, Y[mt]);
-        }
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const E* vp = vb + (((dvt0 + ct) * 4 + mt) * 64 + lane) * 4;
-          f32x4_t v;
-          if constexpr (BF16) {
-            const uint2 r2 = *reinterpret_cast<const uint2*>(vp);
-            v = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                        __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
-          } else {
-            const float4 r4 = *reinterpret_cast<const float4*>(vp);
-            v = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+          for (int mt = 0; mt < 4; ++mt) Y[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        times_S(ka, Y, std::false_type{});
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            f32x4_t v;
+            if constexpr (BF16) {
+              const uint2 r2 = vr[ct][mt];
+              v = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                          __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
+            } else {
+              const float4 r4 = vr[ct][mt];
+              v = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Y[ct][mt][e] = fmaf(-egv[mt][e], Y[ct][mt][e], v[e]);
           }
-          Y[mt] = v - gvec(Gm::G_EG, mt) * Y[mt];
-        }
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) bZ[ct][ks] = Ch::bop(Y[ks * TPS], Y[(ks * TPS + 1) % 4]);
-        fence();
+          for (int ks = 0; ks < KSC; ++ks) bZ[ct][ks] = Ch::bop(Y[ct][ks * TPS], Y[ct][(ks * TPS + 1) % 4]);
+        }
       }
-      // stage 2: O = Q S^T
+      fence();
+      // stage 2: O^T = S Q^T (tile (ct, mt): rows d_v 16 (dvt0 + ct) + 4 g + e,
+      // column token 16 mt + col, so a lane holds four consecutive d_v of one
+      // token: the output goes out as 8-byte stores)
       f32x4_t O[CT][4];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) O[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          const Bop b = bS_of(ct, ks);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) O[ct][mt] = Ch::step(tile(qa, mt * KSD + ks), b, O[ct][mt]);
-        }
-        fence();
-      }
+      times_S(qa, O, std::true_type{});
       // stage 3: U = T diag(beta) Z; U as B operands, plain (for P U) and decayed
       // by e^{G_last - G} (for the state); the checkpoint path keeps U itself
       Bop bU[CT][KSC], bUd[CT][KSC];
       f32x4_t U[CT][4];
+      {
+        uint4 tt[NTRI];
+#pragma unroll
+        for (int t = 0; t < NTRI; ++t) tt[t] = tile(ta, t);
+        fence();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks)
+              if (ks * SK <= 16 * mt + 15) u = Ch::step(tt[TriTiles<BF16>::index(mt, ks)], bZ[ct][ks], u);
+            U[ct][mt] = u;
+          }
+      }
+      uint4 pt[NTRI];
+#pragma unroll
+      for (int t = 0; t < NTRI; ++t) pt[t] = tile(pa, t);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f32x4_t u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KSC; ++ks)
-            if (ks * SK <= 16 * mt + 15) u = Ch::step(tile(ta, TriTiles<BF16>::index(mt, ks)), bZ[ct][ks], u);
-          U[ct][mt] = u;
-        }
         f32x4_t Ud[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Ud[mt] = U[ct][mt] * gvec(Gm::G_D, mt);
@@ -1083,29 +1174,50 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           bU[ct][ks] = Ch::bop(U[ct][ks * TPS], U[ct][(ks * TPS + 1) % 4]);
           bUd[ct][ks] = Ch::bop(Ud[ks * TPS], Ud[(ks * TPS + 1) % 4]);
         }
-        fence();
       }
-      // stage 4: O = diag(e^G) Q S^T + P U
+      fence();
+      // stage 4: O^T = S Q^T diag(e^G) + U^T P^T
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
+      for (int mt = 0; mt < 4; ++mt) {
+        const float e = gt[Gm::G_EG + 16 * mt + col];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f32x4_t o = O[ct][mt] * gvec(Gm::G_EG, mt);
+        for (int ct = 0; ct < CT; ++ct) {
+          f32x4_t o = O[ct][mt] * e;
 #pragma unroll
           for (int ks = 0; ks < KSC; ++ks)
-            if (ks * SK <= 16 * mt + 15) o = Ch::step(tile(pa, TriTiles<BF16>::index(mt, ks)), bU[ct][ks], o);
+            if (ks * SK <= 16 * mt + 15) o = Ch::step_t(bU[ct][ks], pt[TriTiles<BF16>::index(mt, ks)], o);
           O[ct][mt] = o;
         }
       }
-      // O of this chunk: token seq_start + 64 ci + 16 mt + 4 g + i, column 16 (dvt0 + ct) + col
-      E* ob = static_cast<E*>(A.o) + static_cast<size_t>(seq_start + kC * ci + 4 * g) * rowstride + h * D + col;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      // O of this chunk goes out through this wave's own slice of the V region
+      // (read only in stage 1, by this wave): row-major [64 tokens][CT 16 d_v],
+      // then 16-byte stores, whole 32 CT-byte runs of a token row per lane group
+      {
+        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
+        constexpr int RW = CT * 16;                // d_v of a token row in this slice
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * mt + 4 * g + i < clen) ob[(16 * mt + i) * rowstride + 16 * (dvt0 + ct)] = to_e<BF16>(O[ct][mt][i]);
+          for (int ct = 0; ct < CT; ++ct) {
+            E* dst = ol + (16 * mt + col) * RW + 16 * ct + 4 * g;
+            if constexpr (BF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(O[ct][mt][0], O[ct][mt][1]),
+                                                          pack2_bf16(O[ct][mt][2], O[ct][mt][3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(O[ct][mt][0], O[ct][mt][1], O[ct][mt][2], O[ct][mt][3]);
+            }
+          }
+        constexpr int LPR = RW * static_cast<int>(sizeof(E)) / 16;  // lanes per token row
+        constexpr int RPI = 64 / LPR;                               // token rows per instruction
+        E* og = static_cast<E*>(A.o) + static_cast<size_t>(seq_start + kC * ci) * rowstride + h * D + 16 * dvt0 +
+                (lane % LPR) * (16 / sizeof(E));
+#pragma unroll
+        for (int j = 0; j < kC / RPI; ++j) {
+          const int tok = j * RPI + lane / LPR;
+          const uint4 v4 = *reinterpret_cast<const uint4*>(ol + tok * RW + (lane % LPR) * (16 / sizeof(E)));
+          if (tok < clen) *reinterpret_cast<uint4*>(og + static_cast<size_t>(tok) * rowstride) = v4;
+        }
+      }
       fence();
       const float eGl = gt[Gm::G_EGL];
 
@@ -1146,16 +1258,27 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
         }
       }
 
-      // S^T <- e^{G_last} S^T + K^T diag(e^{G_last - G}) U
+      // S^T <- e^{G_last} S^T + K^T diag(e^{G_last - G}) U: all NT x CT
+      // accumulators advance one contraction step at a time, so NT * CT
+      // independent MFMAs are in flight between dependent ones
+      {
+        uint4 ktt[NT][KSC];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          f32x4_t a = st[ct][i] * eGl;
+          for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
 #pragma unroll
-          for (int ks = 0; ks < KSC; ++ks) a = Ch::step(tile(kt, i * KSC + ks), bUd[ct][ks], a);
-          st[ct][i] = a;
-        }
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < NT; ++i) st[ct][i] = st[ct][i] * eGl;
+        fence();
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) st[ct][i] = Ch::step(ktt[i][ks], bUd[ct][ks], st[ct][i]);
+      }
       if (CKPT && A.ckpt_every > 0) {
         const int done = kC * ci + clen;
         if (done % A.ckpt_every == 0)

@@ -98,9 +98,9 @@ def test_workspace_size(gdn):
     n3 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 1 << 20, 8)
     assert n1 > 0 and n2 == n1 and n3 == n1
     # per (chunk slot, k-head): Q, K and K^T (64 x 128 bf16 each); per v-head of
-    # the group: T diag(beta) and P (6 lower-triangle tiles of 16 x 32 each) and a
-    # 1 KB gate tile
-    per_item = 3 * 64 * 128 * 2 + 3 * (2 * 6 * 1024 + 1024)
+    # the group: T diag(beta) and P (6 lower-triangle tiles of 16 x 32 each), a
+    # 1 KB gate tile and V (64 x 128 bf16)
+    per_item = 3 * 64 * 128 * 2 + 3 * (2 * 6 * 1024 + 1024 + 64 * 128 * 2)
     assert abs(n1 - 16 * 16 * per_item) < 256 * 1024
     # a call with fewer chunks than ring slots needs only as many slots
     n4 = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 100, 1)
