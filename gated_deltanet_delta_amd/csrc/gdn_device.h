@@ -101,6 +101,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// The same ordering written out: this wave's LDS operations complete
+// (lgkmcnt), then the barrier; the compiler moves no memory access across
+// it.  Nothing waits for the wave's global loads or stores (vmcnt).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // SiLU and sigmoid with the hardware exp2 and reciprocal (about 2 ulp).  An
 // argument so negative that 2^x underflows gives 1 + 0; so positive that it

@@ -237,6 +237,21 @@ __device__ __forceinline__ uint4 load_l2(const void* base, uint32_t off) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same load written straight into LDS (one 1 KB tile per wave: lane i's
+// 16 bytes land at lds + 16 i), counted by the wave's vector-memory counter.
+__device__ __forceinline__ void load_l2_to_lds(const void* base, uint32_t off, void* lds) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), static_cast<short>(0), 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, off, 0, 0, 1);
+}
+// wait for every vector-memory operation of this wave (s_waitcnt vmcnt(0))
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// wait for every LDS operation of this wave (s_waitcnt lgkmcnt(0))
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // ---------------------------------------------------------------------------
 // plan: sequence table from cu_seqlens; hand-off state cleared
 // ---------------------------------------------------------------------------
@@ -273,7 +288,11 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
       for (int s = 0; s < S; ++s) stab[8 * s + SQ_FLAGS] = 0;
       total = 0;
     }
-    if (total > A.max_chunks) total = 0;  // cannot happen for a valid partition
+    if (total > A.max_chunks) {  // cannot happen for a valid partition
+      report_error(A.dev_err, GDN_DEV_BAD_SEQLENS);
+      for (int s = 0; s < S; ++s) stab[8 * s + SQ_FLAGS] = 0;
+      total = 0;
+    }
     hdr[HDR_TOTAL] = total;
     hdr[HDR_ABORT] = 0;
   }
@@ -963,35 +982,104 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
     const char* ringb = static_cast<const char*>(A.workspace) + Lay.ring;
     // The helper waves walk the same chunks as the compute waves (every valid
-    // sequence's chunks in order): wait for the producer's flag, copy the
-    // item's tiles (the k-head's Q, K, K^T; this v-head's T diag(beta), P,
-    // gates and V) from the L2 into the LDS buffer, and take the barrier.
-    constexpr int NCP = (Gm::STAGE_TILES + NHW - 1) / NHW;  // tiles copied per helper wave
-    int nchunks = 0;
-    for (int s = 0; s < S; ++s)
-      if (stab[8 * s + SQ_FLAGS] & SQF_VALID) nchunks += stab[8 * s + SQ_NCHUNK];
-    for (int c = 0; c < nchunks; ++c) {
-      char* b = buf(c);
+    // sequence's chunks in order).  Right after chunk c's barrier the buffer
+    // of chunk c+1 is free (the compute waves are done with chunk c-1): the
+    // helpers issue loads that write the item's tiles (the k-head's Q, K,
+    // K^T; this v-head's T diag(beta), P, gates and V) straight from the L2
+    // into that buffer, so they land while chunk c is computed.  Before
+    // chunk c+1's barrier each helper wave polls the producer's flag for
+    // chunk c+2, which also waits for its own loads of chunk c+1.
+    // The buffer refilled holds, in its V region, the output of the chunk
+    // NBUF before (written there by the compute waves): each helper wave
+    // first reads the pieces of it that lie in the tiles it then overwrites
+    // itself, and stores them to o.
+    constexpr int NCP = (Gm::STAGE_TILES + NHW - 1) / NHW;  // tiles loaded per helper wave
+    constexpr int RW = CT * 16;            // d_v per compute wave's slice
+    constexpr int VT0 = Gm::HEAD0 + Gm::HV;  // first tile of the V region
+    constexpr int NVP = (Gm::STAGE_TILES - VT0 + NHW - 1) / NHW;  // V tiles per helper wave
+    const int vt_first = VT0 + ((hw - VT0) % NHW + NHW) % NHW;     // first of them
+    const size_t rowstride = static_cast<size_t>(Hv) * D;
+    struct Pieces {
+      uint4 v[NVP];
+    };
+    auto read_out = [&](int c) {
+      Pieces ov;
+#pragma unroll
+      for (int q = 0; q < NVP; ++q) {
+        const int t = min(vt_first + NHW * q, Gm::STAGE_TILES - 1);
+        ov.v[q] = *reinterpret_cast<const uint4*>(buf(c) + static_cast<size_t>(t) * kTileBytes + 16 * lane);
+      }
+      wait_lds();  // read before this wave's loads overwrite the tiles
+      return ov;
+    };
+    auto write_out = [&](int tok0, int clen, const Pieces& ov) {
+      E* og = static_cast<E*>(A.o) + static_cast<size_t>(tok0) * rowstride + h * D;
+#pragma unroll
+      for (int q = 0; q < NVP; ++q) {
+        const int t = vt_first + NHW * q;
+        const int e = ((t - VT0) * kTileBytes + 16 * lane) / static_cast<int>(sizeof(E));
+        const int w = e / (kC * RW), tok = (e % (kC * RW)) / RW, dv = w * RW + e % RW;
+        if (t < Gm::STAGE_TILES && tok < clen)
+          *reinterpret_cast<uint4*>(og + static_cast<size_t>(tok) * rowstride + dv) = ov.v[q];
+      }
+    };
+    auto poll = [&](int c) {
       wait_at_least(ready + ((c % RS) * Hk + kh) * kLine, c + 1, hdr + HDR_ABORT, A.dev_err);
+    };
+    auto fill = [&](int c) {  // chunk c's tiles, ring slot c % RS, into buf(c)
       const char* rb = ringb + (static_cast<size_t>(c % RS) * Hk + kh) * Lay.item_bytes;
-      uint4 rv[NCP];
+      char* b = buf(c);
 #pragma unroll
       for (int j = 0; j < NCP; ++j) {
         const int t = hw + j * NHW;
         const int src = t < Gm::HEAD0 ? t : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0);
-        rv[j] = t < Gm::STAGE_TILES ? load_l2(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane))
-                                    : make_uint4(0, 0, 0, 0);
+        if (t < Gm::STAGE_TILES) load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane), b + static_cast<size_t>(t) * kTileBytes);
       }
-#pragma unroll
-      for (int j = 0; j < NCP; ++j) {
-        const int t = hw + j * NHW;
-        if (t < Gm::STAGE_TILES) *reinterpret_cast<uint4*>(b + static_cast<size_t>(t) * kTileBytes + 16 * lane) = rv[j];
+    };
+    // the walk as a cursor: token offset and length of the next chunk
+    int cur_s = -1, cur_ci = 0, cur_nc = 0, cur_start = 0, cur_len = 0;
+    auto advance = [&]() {
+      ++cur_ci;
+      while (cur_ci >= cur_nc && cur_s + 1 < S) {
+        const int32_t* se = stab + 8 * ++cur_s;
+        cur_ci = 0;
+        cur_nc = (se[SQ_FLAGS] & SQF_VALID) ? se[SQ_NCHUNK] : 0;
+        cur_start = se[SQ_START];
+        cur_len = se[SQ_LEN];
       }
-      lds_barrier();  // chunk c staged
+    };
+    const int total = hdr[HDR_TOTAL];
+    int prev_tok = 0, prev_len = 0;  // chunk c-1
+    if (total > 0) {
+      poll(0);
+      fill(0);
+    }
+    for (int c = 0; c < total; ++c) {
+      advance();
+      const int tok = cur_start + kC * cur_ci, len = min(kC, cur_len - kC * cur_ci);
+      if (NBUF == 2 && c + 1 < total) poll(c + 1);
+      wait_vm();   // this wave's loads of chunk c are in LDS
+      lds_sync();  // chunk c staged
       if (hw == 0 && lane == 0)
         __hip_atomic_store(consumed + h * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (NBUF == 1) lds_barrier();  // the compute waves are done with the buffer
+      if (NBUF == 2) {
+        const Pieces ov = read_out(c - 1 < 0 ? 0 : c - 1);
+        if (c + 1 < total) fill(c + 1);
+        if (c >= 1) write_out(prev_tok, prev_len, ov);
+      } else {
+        lds_sync();  // the compute waves are done with the buffer
+        const Pieces ov = read_out(c);
+        if (c + 1 < total) {
+          poll(c + 1);
+          fill(c + 1);
+        }
+        write_out(tok, len, ov);
+      }
+      prev_tok = tok;
+      prev_len = len;
     }
+    lds_sync();  // the compute waves are done with the last chunk
+    if (NBUF == 2 && total > 0) write_out(prev_tok, prev_len, read_out(total - 1));
     return;
   }
 
@@ -1031,7 +1119,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     };
 
     for (int ci = 0; ci < nc; ++ci, ++c) {
-      lds_barrier();  // chunk c staged
+      lds_sync();  // chunk c staged
       const char* base = buf(c);
       const int clen = min(kC, len - kC * ci);
       const uint4* qa = reinterpret_cast<const uint4*>(base + Gm::QA * kTileBytes);
@@ -1043,12 +1131,15 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       const E* vb = reinterpret_cast<const E*>(base + Gm::V_OFF);
       auto tile = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
 
-      // The step runs in stages separated by scheduling barriers, in the order
-      // that keeps the fewest values live: Y = K S^T -> Z = V - diag(e^G) Y as
-      // B operands; O = Q S^T; U = T diag(beta) Z -> U as B operands (plain
-      // and decayed); O += P U; checkpoints; state update.  Inside a product
-      // the operand tiles of contraction step ks+1 are read from LDS while
-      // the MFMAs of step ks run, and every tile read feeds all CT tiles.
+      // The step is ordered so that VALU work independent of the MFMAs in
+      // flight is issued while they run: Y = K S^T and O^T = S Q^T back to
+      // back; Z = V - diag(e^G) Y (its B operands) and the state's decay under
+      // the O^T products; U = T diag(beta) Z; O^T scaled by e^G under U; U as B
+      // operands (plain and decayed); O^T += U^T P^T and the state update; the
+      // output last.  Scheduling barriers keep that order and bound the live
+      // registers.  Inside a product the operand tiles of contraction step
+      // ks+1 are read from LDS while the MFMAs of step ks run, and every tile
+      // read feeds all CT tiles.
       auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
       // S^T as B operands (and, read the other way, S as A operands), built
       // once for both products of the state
@@ -1091,59 +1182,61 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           }
         }
       };
-      // stage 1: Y = K S^T, then Z = V - diag(e^G) Y as B operands of the T product
-      Bop bZ[CT][KSC];
-      {
-        // V and e^G are read first, so they arrive under the products
-        using VRaw = typename std::conditional<BF16, uint2, float4>::type;
-        VRaw vr[CT][4];
-        f32x4_t egv[4];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((dvt0 + ct) * 4 + mt) * 64 + lane) * 4);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) egv[mt] = gvec(Gm::G_EG, mt);
-        f32x4_t Y[CT][4];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) Y[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        times_S(ka, Y, std::false_type{});
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            f32x4_t v;
-            if constexpr (BF16) {
-              const uint2 r2 = vr[ct][mt];
-              v = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                          __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
-            } else {
-              const float4 r4 = vr[ct][mt];
-              v = f32x4_t{r4.x, r4.y, r4.z, r4.w};
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Y[ct][mt][e] = fmaf(-egv[mt][e], Y[ct][mt][e], v[e]);
-          }
-#pragma unroll
-          for (int ks = 0; ks < KSC; ++ks) bZ[ct][ks] = Ch::bop(Y[ct][ks * TPS], Y[ct][(ks * TPS + 1) % 4]);
-        }
-      }
-      fence();
-      // stage 2: O^T = S Q^T (tile (ct, mt): rows d_v 16 (dvt0 + ct) + 4 g + e,
-      // column token 16 mt + col, so a lane holds four consecutive d_v of one
-      // token: the output goes out as 8-byte stores)
-      f32x4_t O[CT][4];
+      const float eGl = gt[Gm::G_EGL];
+      // Y = K S^T (rows token) and O^T = S Q^T (tile (ct, mt): rows d_v
+      // 16 (dvt0 + ct) + 4 g + e, column token 16 mt + col, so a lane holds
+      // four consecutive d_v of one token)
+      f32x4_t Y[CT][4], O[CT][4];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) O[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) {
+          Y[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          O[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      times_S(ka, Y, std::false_type{});
+      // V and e^G, read under the O^T products
+      using VRaw = typename std::conditional<BF16, uint2, float4>::type;
+      VRaw vr[CT][4];
+      f32x4_t egv[4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((dvt0 + ct) * 4 + mt) * 64 + lane) * 4);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) egv[mt] = gvec(Gm::G_EG, mt);
       times_S(qa, O, std::true_type{});
-      // stage 3: U = T diag(beta) Z; U as B operands, plain (for P U) and decayed
-      // by e^{G_last - G} (for the state); the checkpoint path keeps U itself
-      Bop bU[CT][KSC], bUd[CT][KSC];
+      // Z = V - diag(e^G) Y as B operands of the T product
+      Bop bZ[CT][KSC];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4_t v;
+          if constexpr (BF16) {
+            const uint2 r2 = vr[ct][mt];
+            v = f32x4_t{__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                        __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u)};
+          } else {
+            const float4 r4 = vr[ct][mt];
+            v = f32x4_t{r4.x, r4.y, r4.z, r4.w};
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Y[ct][mt][e] = fmaf(-egv[mt][e], Y[ct][mt][e], v[e]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) bZ[ct][ks] = Ch::bop(Y[ct][ks * TPS], Y[ct][(ks * TPS + 1) % 4]);
+      }
+      // the state's decay (a checkpoint inside the chunk still needs S itself)
+      if constexpr (!CKPT) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < NT; ++i) st[ct][i] = st[ct][i] * eGl;
+      }
+      fence();
+      // U = T diag(beta) Z
       f32x4_t U[CT][4];
       {
         uint4 tt[NTRI];
@@ -1161,9 +1254,19 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
             U[ct][mt] = u;
           }
       }
+      // O^T scaled by e^G (per token column) while U runs; the P and K^T tiles read
       uint4 pt[NTRI];
 #pragma unroll
       for (int t = 0; t < NTRI; ++t) pt[t] = tile(pa, t);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float e = gt[Gm::G_EG + 16 * mt + col];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) O[ct][mt] = O[ct][mt] * e;
+      }
+      fence();
+      // U as B operands: plain (for P U) and decayed by e^{G_last - G} (for the state)
+      Bop bU[CT][KSC], bUd[CT][KSC];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         f32x4_t Ud[4];
@@ -1175,52 +1278,23 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           bUd[ct][ks] = Ch::bop(Ud[ks * TPS], Ud[(ks * TPS + 1) % 4]);
         }
       }
-      fence();
-      // stage 4: O^T = S Q^T diag(e^G) + U^T P^T
+      uint4 ktt[NT][KSC];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float e = gt[Gm::G_EG + 16 * mt + col];
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
+      fence();
+      // O^T += U^T P^T
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          f32x4_t o = O[ct][mt] * e;
+          f32x4_t o = O[ct][mt];
 #pragma unroll
           for (int ks = 0; ks < KSC; ++ks)
             if (ks * SK <= 16 * mt + 15) o = Ch::step_t(bU[ct][ks], pt[TriTiles<BF16>::index(mt, ks)], o);
           O[ct][mt] = o;
         }
-      }
-      // O of this chunk goes out through this wave's own slice of the V region
-      // (read only in stage 1, by this wave): row-major [64 tokens][CT 16 d_v],
-      // then 16-byte stores, whole 32 CT-byte runs of a token row per lane group
-      {
-        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
-        constexpr int RW = CT * 16;                // d_v of a token row in this slice
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            E* dst = ol + (16 * mt + col) * RW + 16 * ct + 4 * g;
-            if constexpr (BF16) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(O[ct][mt][0], O[ct][mt][1]),
-                                                          pack2_bf16(O[ct][mt][2], O[ct][mt][3]));
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(O[ct][mt][0], O[ct][mt][1], O[ct][mt][2], O[ct][mt][3]);
-            }
-          }
-        constexpr int LPR = RW * static_cast<int>(sizeof(E)) / 16;  // lanes per token row
-        constexpr int RPI = 64 / LPR;                               // token rows per instruction
-        E* og = static_cast<E*>(A.o) + static_cast<size_t>(seq_start + kC * ci) * rowstride + h * D + 16 * dvt0 +
-                (lane % LPR) * (16 / sizeof(E));
-#pragma unroll
-        for (int j = 0; j < kC / RPI; ++j) {
-          const int tok = j * RPI + lane / LPR;
-          const uint4 v4 = *reinterpret_cast<const uint4*>(ol + tok * RW + (lane % LPR) * (16 / sizeof(E)));
-          if (tok < clen) *reinterpret_cast<uint4*>(og + static_cast<size_t>(tok) * rowstride) = v4;
-        }
-      }
-      fence();
-      const float eGl = gt[Gm::G_EGL];
-
       // state checkpoints inside this chunk: p = m * every in (64 ci, 64 ci + clen);
       // the state after token r = p - 64 ci - 1 of the chunk is
       // e^{G_r} S + K^T diag(d^(r)) U.  One at the chunk's end is the updated state.
@@ -1258,26 +1332,42 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
         }
       }
 
-      // S^T <- e^{G_last} S^T + K^T diag(e^{G_last - G}) U: all NT x CT
-      // accumulators advance one contraction step at a time, so NT * CT
-      // independent MFMAs are in flight between dependent ones
-      {
-        uint4 ktt[NT][KSC];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-          for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
+      if constexpr (CKPT) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int i = 0; i < NT; ++i) st[ct][i] = st[ct][i] * eGl;
-        fence();
+      }
+      // S^T <- e^{G_last} S^T + K^T diag(e^{G_last - G}) U: all NT x CT
+      // accumulators advance one contraction step at a time, so NT * CT
+      // independent MFMAs are in flight between dependent ones
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
+      for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-          for (int i = 0; i < NT; ++i)
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) st[ct][i] = Ch::step(ktt[i][ks], bUd[ct][ks], st[ct][i]);
+          for (int ct = 0; ct < CT; ++ct) st[ct][i] = Ch::step(ktt[i][ks], bUd[ct][ks], st[ct][i]);
+      fence();
+      // O of this chunk into this wave's own slice of the V region (read only
+      // by this wave, in the step's first products): row-major [64 tokens][CT
+      // 16 d_v].  The helper waves store it to o before the buffer is refilled,
+      // so that no store of this wave has to complete before its registers
+      // are reused.
+      {
+        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
+        constexpr int RW = CT * 16;                // d_v of a token row in this slice
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            E* dst = ol + (16 * mt + col) * RW + 16 * ct + 4 * g;
+            if constexpr (BF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(O[ct][mt][0], O[ct][mt][1]),
+                                                          pack2_bf16(O[ct][mt][2], O[ct][mt][3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(O[ct][mt][0], O[ct][mt][1], O[ct][mt][2], O[ct][mt][3]);
+            }
+          }
       }
       if (CKPT && A.ckpt_every > 0) {
         const int done = kC * ci + clen;
@@ -1285,7 +1375,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           store_state(A.ckpt + (static_cast<size_t>(ckpt0 + done / A.ckpt_every - 1) * Hv + h) * D * D, st);
       }
 
-      if (NBUF == 1) lds_barrier();  // buffer free for the next chunk
+      if (NBUF == 1) lds_sync();  // buffer free for the next chunk
     }
 
     // ---- final state back to the slot ----
@@ -1310,6 +1400,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
         A.conv_pos[slot * kPosStride] = static_cast<int32_t>(pos_end << kPosShift);
     }
   }
+  lds_sync();  // every chunk's O in LDS: the helpers store the last ones
 }
 
 // ---------------------------------------------------------------------------
