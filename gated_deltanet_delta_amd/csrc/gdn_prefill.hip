@@ -337,6 +337,16 @@ struct Chain<true> {
   __device__ static f32x4_t step(uint4 a, const Bop& b, f32x4_t c) {
     return mfma32(__builtin_bit_cast(bf16x8_t, a), b, c);
   }
+  // b's elements scaled: the first four by d0, the last four by d1
+  __device__ static Bop scaled(const Bop& b, const f32x4_t& d0, const f32x4_t& d1) {
+    Bop r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k] = static_cast<__bf16>(static_cast<float>(b[k]) * d0[k]);
+      r[k + 4] = static_cast<__bf16>(static_cast<float>(b[k + 4]) * d1[k]);
+    }
+    return r;
+  }
   // The transposed product: a lane supplies A[row l%16][k-set] and B[k-set][col
   // l%16] in the same register positions, so B-operand registers of X (k, n)
   // are the A operand of X^T (rows n, k) and a packed A tile of Y (rows m, k)
@@ -350,6 +360,7 @@ template <>
 struct Chain<false> {
   using Bop = f32x4_t;
   __device__ static Bop bop(const f32x4_t& t0, const f32x4_t&) { return t0; }
+  __device__ static Bop scaled(const Bop& b, const f32x4_t& d0, const f32x4_t&) { return b * d0; }
   __device__ static f32x4_t step(uint4 a, const Bop& b, f32x4_t c) {
     c = mfma4(__uint_as_float(a.x), b[0], c);
     c = mfma4(__uint_as_float(a.y), b[1], c);
@@ -1278,11 +1289,16 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           bUd[ct][ks] = Ch::bop(Ud[ks * TPS], Ud[(ks * TPS + 1) % 4]);
         }
       }
+      // K^T tiles for the state update (read after the checkpoints when
+      // there are any, which take them from LDS themselves)
       uint4 ktt[NT][KSC];
+      auto load_ktt = [&] {
 #pragma unroll
-      for (int i = 0; i < NT; ++i)
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
+          for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
+      };
+      if constexpr (!CKPT) load_ktt();
       fence();
       // O^T += U^T P^T
 #pragma unroll
@@ -1295,6 +1311,28 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
             if (ks * SK <= 16 * mt + 15) o = Ch::step_t(bU[ct][ks], pt[TriTiles<BF16>::index(mt, ks)], o);
           O[ct][mt] = o;
         }
+      // O of this chunk into this wave's own slice of the V region (read only
+      // by this wave, in the step's first products): row-major [64 tokens][CT
+      // 16 d_v].  The helper waves store it to o before the buffer is refilled,
+      // so that no store of this wave has to complete before its registers
+      // are reused.
+      auto write_o = [&] {
+        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
+        constexpr int RW = CT * 16;                // d_v of a token row in this slice
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            E* dst = ol + (16 * mt + col) * RW + 16 * ct + 4 * g;
+            if constexpr (BF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(O[ct][mt][0], O[ct][mt][1]),
+                                                          pack2_bf16(O[ct][mt][2], O[ct][mt][3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(O[ct][mt][0], O[ct][mt][1], O[ct][mt][2], O[ct][mt][3]);
+            }
+          }
+      };
+      if constexpr (CKPT) write_o();  // O is not kept live across the checkpoints
       // state checkpoints inside this chunk: p = m * every in (64 ci, 64 ci + clen);
       // the state after token r = p - 64 ci - 1 of the chunk is
       // e^{G_r} S + K^T diag(d^(r)) U.  One at the chunk's end is the updated state.
@@ -1318,8 +1356,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           for (int ct = 0; ct < CT; ++ct) {
             Bop bR[KSC];
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-              bR[ks] = Ch::bop(U[ct][ks * TPS] * dr[ks * TPS], U[ct][(ks * TPS + 1) % 4] * dr[(ks * TPS + 1) % 4]);
+            for (int ks = 0; ks < KSC; ++ks) bR[ks] = Ch::scaled(bU[ct][ks], dr[ks * TPS], dr[(ks * TPS + 1) % 4]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
               f32x4_t a = st[ct][i] * eGr;
@@ -1333,6 +1370,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       }
 
       if constexpr (CKPT) {
+        load_ktt();
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1348,27 +1386,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) st[ct][i] = Ch::step(ktt[i][ks], bUd[ct][ks], st[ct][i]);
       fence();
-      // O of this chunk into this wave's own slice of the V region (read only
-      // by this wave, in the step's first products): row-major [64 tokens][CT
-      // 16 d_v].  The helper waves store it to o before the buffer is refilled,
-      // so that no store of this wave has to complete before its registers
-      // are reused.
-      {
-        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
-        constexpr int RW = CT * 16;                // d_v of a token row in this slice
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            E* dst = ol + (16 * mt + col) * RW + 16 * ct + 4 * g;
-            if constexpr (BF16) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(O[ct][mt][0], O[ct][mt][1]),
-                                                          pack2_bf16(O[ct][mt][2], O[ct][mt][3]));
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(O[ct][mt][0], O[ct][mt][1], O[ct][mt][2], O[ct][mt][3]);
-            }
-          }
-      }
+      if constexpr (!CKPT) write_o();
       if (CKPT && A.ckpt_every > 0) {
         const int done = kC * ci + clen;
         if (done % A.ckpt_every == 0)
