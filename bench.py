@@ -20,7 +20,9 @@ roofline fractions.
 `prefill_varlen` times one call of the variable-length batched prefill (4
 sequences with the seeded lengths of that workload, about 101 K tokens).
 `prefill_ckpt` times the T = 8192 prefill that also writes the state every 512
-tokens, beside the same prefill without checkpoints.  `decode_batch` times the
+tokens (block ends on chunk boundaries) and every 528 tokens (the hybrid
+model's block, ending inside chunks), each beside the same prefill without
+checkpoints.  `decode_batch` times the
 decode step at 16, 64 and 256 slots (graph replays over cold pools), each
 beside a plain device copy of the same state bytes.  `verify_economics` times
 verify(k) for k = 1 .. 4 and turns it, with rollback and decode, into the cost
@@ -52,7 +54,7 @@ DECODE_BYTES = 26_116_864                      # cfg: 4 slots x 1 token
 DECODE_STATE_BYTES = 25_165_824                # state read + write
 VERIFY_BYTES = 64_752_640                      # 4 slots x k = 4, snapshots written
 ROLLBACK_BYTES_PER_SLOT = 6_291_456
-CKPT_EVERY = 512                               # tokens between state checkpoints
+CKPT_EVERY = (512, 528)                        # tokens between state checkpoints
 DECODE_SWEEP = (16, 64, 256)                   # decode batch sizes of the sweep
 STACK_LAYERS = 36                              # GDN layers of the stack figure
 
@@ -504,35 +506,37 @@ def main():
                   "us": round(ms_vl * 1e3, 1), "tokens_per_s": round(n_vl / (ms_vl * 1e-3), 1)}
         del lx, la, lb, lo, lws, lpool
     # The T = 8192 prefill that also writes a state checkpoint every 512 tokens
-    # (16 checkpoints of 3 MiB), against the same prefill without them, both
-    # timed the same way (event pair around back-to-back calls).
+    # (16 checkpoints of 3 MiB, at chunk ends) and every 528 tokens (15, inside
+    # chunks), against the same prefill without them, both timed the same way
+    # (event pair around back-to-back calls).
     ckpt_fig = None
     if not args.no_ckpt:
-        every = CKPT_EVERY
-        ck = torch.empty(T_PREFILL // every, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+        ckpt_fig = []
         f_plain = lambda i: gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err)
-        f_ck = lambda i: gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err,
-                                             ckpt=ck, ckpt_every=every)
-        f_ck(0)
-        torch.cuda.synchronize()
-        # the last checkpoint of a sequence that ends on a boundary is its final state
-        if not torch.equal(ck[-1], ppool.state[int(pslot[0])]):
-            print(json.dumps({"error": "the last checkpoint differs from the final state"}))
-            sys.exit(4)
-        # alternate the two loops so that clock and thermal drift hit both alike
-        t_plain, t_ck = [], []
-        for _ in range(6):
-            t_plain.append(loop_ms(f_plain, 5))
-            t_ck.append(loop_ms(f_ck, 5))
-        ms_plain, ms_ck = float(np.median(t_plain)), float(np.median(t_ck))
-        if int(err.item()) != 0:
-            print(json.dumps({"error": f"device error code {int(err.item())} in the checkpoint prefill"}))
-            sys.exit(3)
-        ck_bytes = ck.numel() * 4
-        ckpt_fig = {"every": every, "n_ckpt": int(ck.shape[0]), "ckpt_bytes": ck_bytes,
-                    "us": round(ms_ck * 1e3, 1), "plain_us": round(ms_plain * 1e3, 1),
-                    "overhead_pct": round(100.0 * (ms_ck - ms_plain) / ms_plain, 2)}
-        del ck
+        for every in CKPT_EVERY:
+            ck = torch.empty(T_PREFILL // every, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+            f_ck = lambda i: gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err,
+                                                 ckpt=ck, ckpt_every=every)
+            f_ck(0)
+            torch.cuda.synchronize()
+            # the last checkpoint of a sequence that ends on a boundary is its final state
+            if T_PREFILL % every == 0 and not torch.equal(ck[-1], ppool.state[int(pslot[0])]):
+                print(json.dumps({"error": "the last checkpoint differs from the final state"}))
+                sys.exit(4)
+            # alternate the two loops so that clock and thermal drift hit both alike
+            t_plain, t_ck = [], []
+            for _ in range(6):
+                t_plain.append(loop_ms(f_plain, 5))
+                t_ck.append(loop_ms(f_ck, 5))
+            ms_plain, ms_ck = float(np.median(t_plain)), float(np.median(t_ck))
+            if int(err.item()) != 0:
+                print(json.dumps({"error": f"device error code {int(err.item())} in the checkpoint prefill"}))
+                sys.exit(3)
+            ck_bytes = ck.numel() * 4
+            ckpt_fig.append({"every": every, "n_ckpt": int(ck.shape[0]), "ckpt_bytes": ck_bytes,
+                             "us": round(ms_ck * 1e3, 1), "plain_us": round(ms_plain * 1e3, 1),
+                             "overhead_pct": round(100.0 * (ms_ck - ms_plain) / ms_plain, 2)})
+            del ck
     # Decode at larger batches: B slots x 1 token over cold pools, as graph
     # replays, beside a plain device copy of the same state bytes (read B x
     # 3 MiB, write B x 3 MiB) between cold buffers -- what the memory system

@@ -55,15 +55,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-// Largest number of workgroups one decode call puts on one slot; the
-// position shares must each be at least one unit.
-int step_wgs_per_slot(const gdn_geometry& g) {
-  const int D = g.d_k;
-  const int lpr = D / 4, rpw = 64 / lpr, np = D >= 64 ? 4 : (D >= 32 ? 2 : 1);
-  const int rows_wave = rpw * np;
-  const int nw = (D / rows_wave) < 4 ? (D / rows_wave) : 4;
-  return g.n_v_heads * (D / (nw * rows_wave));
-}
+// Workgroups one decode call puts on one slot; the position shares must
+// each be at least one unit.
+int step_wgs_per_slot(const gdn_geometry& g) { return gdn::decode_wgs_per_slot(g.d_k, g.n_v_heads); }
 
 gdn_status check_geometry(const gdn_geometry* g) {
   if (!g) return fail(GDN_ERR_NULL, "geometry: NULL, required: a gdn_geometry");

@@ -10,6 +10,37 @@
 namespace gdn {
 
 // Arguments of the per-token kernels (decode, verify, conv step, rollback).
+// Work split of the decode and verify step: one workgroup per (batch row,
+// v-head, block of state rows); a state row (d_k floats) is read by LPR lanes
+// as one f32x4 each.  Shared by the kernels and by the host's launch checks.
+template <int D, bool VERIFY>
+struct StepShape {
+  static constexpr int kWaveLanes = 64;
+  static constexpr int LPR = D / 4;                   // lanes per state row (one f32x4 each)
+  static constexpr int RPW = kWaveLanes / LPR;        // rows one wave covers per pass
+  static constexpr int NP = D >= 64 ? 4 : (D >= 32 ? 2 : 1);  // passes per wave
+  static constexpr int ROWS_WAVE = RPW * NP;
+  static constexpr int NW_MAX = D / ROWS_WAVE;
+  // waves per workgroup.  Decode: 8 (64 rows), which halves the workgroups
+  // that add a share of the slot's position with one contended atomic;
+  // verify (no position update, k drafts per workgroup): 4.
+  static constexpr int NW = NW_MAX < (VERIFY ? 4 : 8) ? NW_MAX : (VERIFY ? 4 : 8);
+  static constexpr int ROWS_WG = NW * ROWS_WAVE;
+  static constexpr int WG_PER_HEAD = D / ROWS_WG;
+  static constexpr int THREADS = NW * kWaveLanes;
+};
+
+// workgroups of one decode call on one slot (d_k = 16, 32, 64 or 128; 0 otherwise)
+inline int decode_wgs_per_slot(int d_k, int n_v_heads) {
+  switch (d_k) {
+    case 16: return n_v_heads * StepShape<16, false>::WG_PER_HEAD;
+    case 32: return n_v_heads * StepShape<32, false>::WG_PER_HEAD;
+    case 64: return n_v_heads * StepShape<64, false>::WG_PER_HEAD;
+    case 128: return n_v_heads * StepShape<128, false>::WG_PER_HEAD;
+    default: return 0;
+  }
+}
+
 struct StepArgs {
   float* state;          // decode: in/out; verify: in; rollback: out
   float* conv_state;

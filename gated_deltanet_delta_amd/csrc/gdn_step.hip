@@ -23,22 +23,6 @@
 
 namespace gdn {
 
-template <int D, bool VERIFY>
-struct StepShape {
-  static constexpr int LPR = D / 4;              // lanes per state row (one f32x4 each)
-  static constexpr int RPW = kWave / LPR;        // rows one wave covers per pass
-  static constexpr int NP = D >= 64 ? 4 : (D >= 32 ? 2 : 1);  // passes per wave
-  static constexpr int ROWS_WAVE = RPW * NP;
-  static constexpr int NW_MAX = D / ROWS_WAVE;
-  // waves per workgroup.  Decode: 8 (64 rows), which halves the workgroups
-  // that add a share of the slot's position with one contended atomic;
-  // verify (no position update, k drafts per workgroup): 4.
-  static constexpr int NW = NW_MAX < (VERIFY ? 4 : 8) ? NW_MAX : (VERIFY ? 4 : 8);
-  static constexpr int ROWS_WG = NW * ROWS_WAVE;
-  static constexpr int WG_PER_HEAD = D / ROWS_WG;
-  static constexpr int THREADS = NW * kWave;
-};
-
 // Input of the conv window at relative token `rel` (rel >= 0: token rel of
 // this batch row; rel < 0: ring row of position pos + rel).
 template <bool BF16>
@@ -100,12 +84,12 @@ __device__ __forceinline__ float dot4v(f32x4_t a, float4 b) {
 // Memory order of a call: the slot id and everything that does not depend on
 // it (this token's inputs, conv weights, gates) are requested first; then the
 // ring position; then the state rows (pinned ahead of all arithmetic by a
-// scheduling barrier, so their HBM latency overlaps the rest); then the W-1
-// ring rows of the conv window.
-// RING8: the conv ring has exactly 8 rows, so all of them are read together
-// with the state (no wait on the position before the ring loads) and the
-// window rows are picked in registers.
-template <int D, bool BF16, bool VERIFY, int W, bool RING8>
+// scheduling barrier, so their HBM latency overlaps the rest), with
+// non-temporal loads (each state row is read once per call); then the W-1
+// ring rows of the conv window.  (Reading all ring rows before the state, to
+// skip the wait on the position, measured slower: it puts the ring's bytes
+// ahead of the state's in the memory queues.)
+template <int D, bool BF16, bool VERIFY, int W>
 __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(StepArgs A) {
   using Sh = StepShape<D, VERIFY>;
   constexpr int LPR = Sh::LPR;
@@ -162,40 +146,18 @@ __global__ __launch_bounds__((StepShape<D, VERIFY>::THREADS)) void step_kernel(S
   f32x4_t S[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
-    S[p] = load4(Sg + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4);
+    S[p] = load_nt4(Sg + static_cast<size_t>(row0 + p * Sh::RPW) * D + c4);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- conv window history of this thread's channels: ring rows pos-3 .. pos-1 ----
   float hq[3] = {0.f, 0.f, 0.f}, hv[3] = {0.f, 0.f, 0.f};
   if constexpr (W == 4) {
     const float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
-    if constexpr (RING8) {
-      float rq[8], rv[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        rq[r] = ring[static_cast<size_t>(r) * C + chq];
-        rv[r] = ring[static_cast<size_t>(r) * C + chv];
-      }
-      const uint32_t pu = __builtin_amdgcn_readfirstlane(pos);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const uint32_t r = (pu + static_cast<uint32_t>(t - 3)) & 7u;
-        float a = rq[0], c = rv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-          a = r == static_cast<uint32_t>(i) ? rq[i] : a;
-          c = r == static_cast<uint32_t>(i) ? rv[i] : c;
-        }
-        hq[t] = a;
-        hv[t] = c;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const float* rr = ring + static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(t - 3), R)) * C;
-        hq[t] = rr[chq];
-        hv[t] = rr[chv];
-      }
+    for (int t = 0; t < 3; ++t) {
+      const float* rr = ring + static_cast<size_t>(ring_row(pos + static_cast<uint32_t>(t - 3), R)) * C;
+      hq[t] = rr[chq];
+      hv[t] = rr[chv];
     }
   }
   const bool qk_writer = fe_qk && (h % G == 0) && hb == 0 && slot_ok;
@@ -420,9 +382,8 @@ template <int D, bool BF16, bool VERIFY>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
   using Sh = StepShape<D, VERIFY>;
   dim3 grid(a.Hv * Sh::WG_PER_HEAD, a.batch);
-  if (a.W == 4 && a.R == 8) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, true>), grid, dim3(Sh::THREADS), 0, s, a);
-  else if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4, false>), grid, dim3(Sh::THREADS), 0, s, a);
-  else if (a.W == 0) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 0, false>), grid, dim3(Sh::THREADS), 0, s, a);
+  if (a.W == 4) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 4>), grid, dim3(Sh::THREADS), 0, s, a);
+  else if (a.W == 0) hipLaunchKernelGGL((step_kernel<D, BF16, VERIFY, 0>), grid, dim3(Sh::THREADS), 0, s, a);
   else return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipGetLastError());
 }
