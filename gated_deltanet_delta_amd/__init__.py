@@ -26,7 +26,7 @@ POS_ONE = 65536
 POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
-ABI_VERSION = 4  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
+ABI_VERSION = 5  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
 DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
@@ -80,6 +80,8 @@ _SIGS = {
     "gdn_prefill_chunked_ckpt": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _I, _P,
                                                 ctypes.c_size_t, _P, _P]),
+    "gdn_prefill_chunked_static": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  _P, _P, _I, _I, _I, _P, _P, _P]),
     "gdn_verify_k": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
                                     _P, _P, _P, _P]),
     "gdn_rollback": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _I, _I, _P, _P]),
@@ -398,6 +400,32 @@ def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens,
                                      _ptr(workspace), nbytes, _ptr(o), _ptr(dev_err), _stream(stream)))
 
 
+def prefill_chunked_static(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens, slot, has_init, o,
+                           dev_err=None, stream=None):
+    """gdn_prefill_chunked_static: prefill_chunked with the library's own static
+    workspace (no allocation in the call; calls that overlap on one GPU race)."""
+    N = x.shape[0]
+    S = slot.shape[0]
+    C, Hv, dv = geom.conv_channels, geom.n_v_heads, geom.d_v
+    _check_pool(geom, pool)
+    _need(x, "x", (N, C), geom.dtype)
+    _need(a, "a", (N, Hv), geom.dtype)
+    _need(b, "b", (N, Hv), geom.dtype)
+    _need(conv_w, "conv_w", (C, geom.conv_width), torch.float32, optional=geom.conv_width == 0)
+    _need(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32)
+    _need(slot, "slot", (S,), torch.int32)
+    _need(has_init, "has_init", (S,), torch.int32)
+    _need(o, "o", (N, Hv, dv), geom.dtype)
+    _need(dev_err, "dev_err", (1,), torch.int32, optional=True)
+    if dev_err is None:
+        dev_err = _default_err(x.device)
+    g = geom.c_struct()
+    _check(lib().gdn_prefill_chunked_static(ctypes.byref(g), _ptr(pool.state), _ptr(pool.conv_state),
+                                            _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w),
+                                            _ptr(cu_seqlens), _ptr(slot), _ptr(has_init), S, N, CHUNK,
+                                            _ptr(o), _ptr(dev_err), _stream(stream)))
+
+
 def checkpoint_count(seq_lens, ckpt_every: int) -> int:
     """Checkpoints gdn_prefill_chunked_ckpt writes for these sequence lengths."""
     return sum(int(n) // ckpt_every for n in seq_lens)
@@ -405,7 +433,7 @@ def checkpoint_count(seq_lens, ckpt_every: int) -> int:
 
 __all__ = [
     "Geometry", "GdnGeometry", "GdnError", "SlotPool", "lib", "conv_state_step", "decode_step", "verify_k",
-    "rollback", "verify_k_slots", "commit_slots", "prefill_chunked", "prefill_workspace_bytes", "alloc_prefill_workspace",
+    "rollback", "verify_k_slots", "commit_slots", "prefill_chunked", "prefill_chunked_static", "prefill_workspace_bytes", "alloc_prefill_workspace",
     "checkpoint_count", "POS_ONE", "CHUNK",
     "DEV_OK", "DEV_BAD_SLOT", "DEV_BAD_ACCEPTED", "DEV_BAD_SEQLENS", "DEV_WAIT_TIMEOUT", "DEV_BAD_K",
     "DEV_INCOMPLETE", "device_error",

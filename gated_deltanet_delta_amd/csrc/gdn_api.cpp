@@ -387,6 +387,28 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
                       "gdn_prefill_chunked");
 }
 
+gdn_status gdn_prefill_chunked_static(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
+                                      const void* x, const void* a_in, const void* b_in, const float* conv_w,
+                                      const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
+                                      int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* o, int32_t* dev_err,
+                                      void* stream) {
+  const char* name = "gdn_prefill_chunked_static";
+  gdn_status s = check_geometry(g);
+  if (s != GDN_OK) return s;
+  const size_t need = gdn_prefill_workspace_bytes(g, n_tokens, n_seqs);
+  if (need > GDN_PREFILL_STATIC_WORKSPACE_BYTES)
+    return fail(GDN_ERR_WORKSPACE,
+                "workspace: this call needs %zu bytes, the static workspace holds %zu; call gdn_prefill_chunked "
+                "with a workspace of its own",
+                need, static_cast<size_t>(GDN_PREFILL_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  const int e = gdn::prefill_static_workspace(stream, &ws);
+  if (e != 0) return fail(GDN_ERR_LAUNCH, "%s: static workspace address not available (HIP error %d)", name, e);
+  return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
+                      n_tokens, chunk, ws, GDN_PREFILL_STATIC_WORKSPACE_BYTES, o, 0, nullptr, 0, dev_err, stream,
+                      name);
+}
+
 gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
                                     const void* x, const void* a_in, const void* b_in, const float* conv_w,
                                     const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,

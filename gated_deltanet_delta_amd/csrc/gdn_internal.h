@@ -115,5 +115,8 @@ int launch_conv_step(const StepArgs& a, bool bf16, void* stream);
 int launch_rollback(const StepArgs& a, void* stream);
 int launch_commit_slots(const StepArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, bool bf16, void* stream);
+// Device address of the library's static prefill workspace on the GPU of
+// `stream` (GDN_PREFILL_STATIC_WORKSPACE_BYTES); a HIP error code, 0 on success.
+int prefill_static_workspace(void* stream, void** ptr);
 
 }  // namespace gdn

@@ -63,6 +63,8 @@
 // the packed A tile of the transposed product.
 #include <type_traits>
 
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -1502,6 +1504,43 @@ static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st) {
     e = static_cast<int>(hipGetLastError());
     if (e) return e;
   }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// The workspace of the prefill that allocates nothing: a static array, one per
+// GPU, held until the process ends.  Host code uses only the device address
+// looked up per GPU, never the array's name (a host-side stand-in).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[GDN_PREFILL_STATIC_WORKSPACE_BYTES];
+
+int prefill_static_workspace(void* stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return static_cast<int>(e);
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return static_cast<int>(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (p == nullptr) return static_cast<int>(hipErrorInvalidSymbol);
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
   return 0;
 }
 

@@ -82,8 +82,11 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
-                              checkpoints at any block size, GDN_DEV_INCOMPLETE */
+#define GDN_ABI_VERSION 5  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
+                              checkpoints at any block size, GDN_DEV_INCOMPLETE;
+                              5: gdn_prefill_chunked_static */
+/* bytes of the library's own prefill workspace, one per GPU (gdn_prefill_chunked_static) */
+#define GDN_PREFILL_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
 #define GDN_POS_ONE 65536
 #define GDN_POS_STRIDE 32 /* int32 words per slot in conv_pos */
 
@@ -214,6 +217,30 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
                                const int32_t* slot, const int32_t* has_init, int32_t n_seqs,
                                int32_t n_tokens, int32_t chunk, void* workspace,
                                size_t workspace_bytes, void* o, int32_t* dev_err, void* stream);
+
+/*
+ * gdn_prefill_chunked for callers that cannot allocate device memory (code
+ * under graph capture that may not call the allocator, serving loops and
+ * harnesses that forbid allocation): the same computation and results, bit
+ * for bit, with no workspace argument.  The hand-off buffers live in a static
+ * device array of GDN_PREFILL_STATIC_WORKSPACE_BYTES (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends; its address on a GPU
+ * is looked up once, on the first call there.  The call allocates nothing.
+ * The GPU is the one `stream` belongs to (the current device for the null
+ * stream).  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (two streams, two host threads) race and must be ordered, e.g.
+ * on one stream; every call clears the flags it uses before its main launch.
+ * Errors as gdn_prefill_chunked, with GDN_ERR_WORKSPACE when
+ * gdn_prefill_workspace_bytes(g, n_tokens, n_seqs) exceeds the array (the
+ * 16 k-head, 48 v-head, d = 128 bf16 geometry needs about 34 MB at any
+ * n_tokens) and GDN_ERR_LAUNCH when the array's address cannot be had.
+ */
+gdn_status gdn_prefill_chunked_static(const gdn_geometry* g, float* state, float* conv_state,
+                                      int32_t* conv_pos, const void* x, const void* a, const void* b,
+                                      const float* conv_w, const int32_t* cu_seqlens,
+                                      const int32_t* slot, const int32_t* has_init, int32_t n_seqs,
+                                      int32_t n_tokens, int32_t chunk, void* o, int32_t* dev_err,
+                                      void* stream);
 
 /*
  * gdn_prefill_chunked that also writes state checkpoints at block boundaries

@@ -166,6 +166,25 @@ def test_prefill_refusals(gdn):
     assert "d_k: 128 with dtype_in GDN_F32" in L.gdn_last_error().decode()
 
 
+def test_prefill_static_refusals(gdn):
+    """The prefill without a workspace refuses, before touching any GPU, a call
+    whose hand-off buffers would not fit the library's static workspace."""
+    L = gdn.lib()
+    g = _geom(gdn, n_k_heads=64, n_v_heads=192)
+    need = L.gdn_prefill_workspace_bytes(ctypes.byref(g), 8192, 1)
+    cap = 64 << 20
+    assert need > cap
+
+    def call(n_tokens=8192):
+        return L.gdn_prefill_chunked_static(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                                            _p(), 1, n_tokens, 64, _p(), None, None)
+    assert call() == 6
+    msg = L.gdn_last_error().decode()
+    assert f"needs {need} bytes, the static workspace holds {cap}" in msg
+    g.n_v_heads = 100  # not a multiple of n_k_heads: the geometry is refused first
+    assert call() == 3
+
+
 def test_prefill_checkpoint_refusals(gdn):
     L = gdn.lib()
     g = _geom(gdn)
