@@ -129,28 +129,29 @@ def test_checkpoints_fp32():
         _same_as_plain(g, inp, pool, o)
 
 
-def test_checkpoints_full_geometry_sampled_heads():
-    """48 v-heads at d = 128 (one persistent chain launch), 1100 tokens, a
-    checkpoint every 512 tokens."""
+@pytest.mark.parametrize("every", [512, 528])
+def test_checkpoints_full_geometry_all_heads(every):
+    """48 v-heads at d = 128, 1100 tokens, a checkpoint every 512 tokens (on
+    chunk ends) or every 528 (the hybrid model's cache block, inside chunks);
+    every head of every checkpoint against the oracle."""
     g = dataclasses.replace(gi.GEOM_QWEN, n_slots=2)
     inp = gi.prefill_inputs(seed=611, geom=g, lengths=[1100], init_state=True, a_mean=-2.0)
-    pool, o, ckpt, err = _run(g, inp, 512)
+    pool, o, ckpt, err = _run(g, inp, every)
     assert err == 0
-    _check_ckpts(g, inp, 512, ckpt, heads=[0, 1, 2, 47])
+    _check_ckpts(g, inp, every, ckpt)
     _same_as_plain(g, inp, pool, o)
 
 
-@pytest.mark.parametrize("lengths", [[1100, 70], [600, 700]])
+@pytest.mark.parametrize("lengths", [[600, 70], [300, 400]])
 def test_checkpoints_segmented_launches(lengths):
-    """96 v-heads: the chain runs as 16-chunk launch segments, one chain
-    workgroup set per sequence; checkpoints inside a segment, on a segment's
-    last chunk (1024 tokens), and in both sequences of one launch (the second
-    sequence's numbered after the first's)."""
-    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=16, n_v_heads=96, n_slots=2)
+    """32 k-heads x 8 v-heads: two launches over k-head ranges; checkpoints
+    every 256 tokens in both sequences (the second sequence's numbered after
+    the first's), heads on both sides of the split."""
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=32, n_v_heads=256, n_slots=2)
     inp = gi.prefill_inputs(seed=612 + lengths[1], geom=g, lengths=lengths, init_state=True, a_mean=-2.0)
     pool, o, ckpt, err = _run(g, inp, 256)
     assert err == 0
-    _check_ckpts(g, inp, 256, ckpt, heads=[0, 13, 95])
+    _check_ckpts(g, inp, 256, ckpt, heads=[0, 191, 192, 255])
 
 
 def test_resume_from_a_checkpoint_continues_the_request():
