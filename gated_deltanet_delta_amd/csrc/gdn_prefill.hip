@@ -490,14 +490,19 @@ template <bool BF16>
 struct Rows {
   using RawT = typename std::conditional<BF16, uint32_t, uint2>::type;
   RawT r[19];
+  float4 w[2];  // conv weights of the two channels
 };
 
-template <bool BF16>
+template <bool BF16, int KW>
 __device__ __forceinline__ void load_rows(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp, Rows<BF16>& raw) {
   using E = typename Pk<BF16>::E;
   using RawT = typename Rows<BF16>::RawT;
   const E* x = static_cast<const E*>(A.x);
   const int C = A.C;
+  if constexpr (KW == 4) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) raw.w[v] = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
+  }
   const int tfirst = cp.t0 + tq - 3;
   if (tfirst >= cp.seq_start && tq + 16 <= cp.len) {
     const E* xr = x + static_cast<size_t>(tfirst) * C + c0;
@@ -528,7 +533,7 @@ __device__ __forceinline__ void conv_rows(const PrefillArgs& A, int c0, int tq, 
   if constexpr (KW == 4) {
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const float4 w4 = *reinterpret_cast<const float4*>(A.conv_w + (c0 + v) * 4);
+      const float4 w4 = raw.w[v];
       w[v][0] = kNegLog2e * w4.x; w[v][1] = kNegLog2e * w4.y;
       w[v][2] = kNegLog2e * w4.z; w[v][3] = kNegLog2e * w4.w;
     }
@@ -570,14 +575,6 @@ __device__ __forceinline__ void conv_rows(const PrefillArgs& A, int c0, int tq, 
       y[v][r] = tq + r < cp.len ? yy : 0.f;
     }
   }
-}
-
-template <bool BF16, int KW>
-__device__ __forceinline__ void conv_quarter(const PrefillArgs& A, int c0, int tq, const ChunkPos& cp,
-                                             float (&y)[2][16]) {
-  Rows<BF16> raw;
-  load_rows<BF16>(A, c0, tq, cp, raw);
-  conv_rows<BF16, KW>(A, c0, tq, cp, raw, y);
 }
 
 __device__ __forceinline__ ChunkPos chunk_pos(const int32_t* se, int ci) {
@@ -689,36 +686,64 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
 
   // ---- conv + SiLU: item = (2 channels, 16 tokens); the q | k items first
   // (outputs to LDS), then the v items of the group's heads (V straight to the
-  // ring in accumulator layout).  Each round of kThreads items is all of one
-  // kind, so no wave runs both paths in one round. ----
+  // ring in accumulator layout).  A thread takes items tid, tid + kThreads,
+  // ...; the input rows of up to three of its items (two with fp32 inputs)
+  // are requested together before any of them is used, so the loads'
+  // latency is paid once per batch of rounds, not once per round. ----
   {
     constexpr int NQK = 4 * D;             // 2 D channels / 2 per item x 4 quarters
+    constexpr int NB = BF16 ? 3 : 2;       // rounds whose loads are in flight together
     const int n_items = NQK + 2 * G * D;   // + G D v channels / 2 x 4 quarters
-    for (int item = tid; item < n_items; item += kThreads) {
-      float y[2][16];
+    auto item_c0 = [&](int item, int& tq) {
       if (item < NQK) {
         const int q = item / D, cc0 = 2 * (item % D);
-        const int c0 = cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
-        conv_quarter<BF16, KW>(A, c0, 16 * q, cp, y);
+        tq = 16 * q;
+        return cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
+      }
+      const int i2 = item - NQK;
+      tq = 16 * (i2 / (G * D / 2));
+      return 2 * Hk * D + kh * G * D + 2 * (i2 % (G * D / 2));
+    };
+    for (int base = 0; base < n_items; base += NB * kThreads) {
+      Rows<BF16> raw[NB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          *reinterpret_cast<float2*>(qk + (16 * q + r) * QK_LD + cc0) = make_float2(y[0][r], y[1][r]);
-      } else {
-        const int i2 = item - NQK;
-        const int q = i2 / (G * D / 2), vc = 2 * (i2 % (G * D / 2));   // v channel within the group
-        const int hi = vc / D, dv0 = vc % D;
-        conv_quarter<BF16, KW>(A, 2 * Hk * D + kh * G * D + vc, 16 * q, cp, y);
-        E* vb = reinterpret_cast<E*>(htile(hi, Gm::HV) - 16 * lane);
+      for (int k = 0; k < NB; ++k) {
+        const int item = base + k * kThreads + tid;
+        if (item < n_items) {
+          int tq;
+          const int c0 = item_c0(item, tq);
+          load_rows<BF16, KW>(A, c0, tq, cp, raw[k]);
+        }
+      }
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          E* dst = vb + (((dv0 >> 4) * 4 + q) * 64 + g4 * 16 + (dv0 & 15)) * 4;
-          if constexpr (BF16) {
-            *reinterpret_cast<uint4*>(dst) =
-                make_uint4(pack2_bf16(y[0][4 * g4], y[0][4 * g4 + 1]), pack2_bf16(y[0][4 * g4 + 2], y[0][4 * g4 + 3]),
-                           pack2_bf16(y[1][4 * g4], y[1][4 * g4 + 1]), pack2_bf16(y[1][4 * g4 + 2], y[1][4 * g4 + 3]));
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(y[0][4 * g4], y[0][4 * g4 + 1], y[0][4 * g4 + 2], y[0][4 * g4 + 3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(y[1][4 * g4], y[1][4 * g4 + 1], y[1][4 * g4 + 2], y[1][4 * g4 + 3]);
+      for (int k = 0; k < NB; ++k) {
+        const int item = base + k * kThreads + tid;
+        if (item >= n_items) continue;
+        int tq;
+        const int c0 = item_c0(item, tq);
+        float y[2][16];
+        conv_rows<BF16, KW>(A, c0, tq, cp, raw[k], y);
+        if (item < NQK) {
+          const int cc0 = 2 * (item % D);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<float2*>(qk + (tq + r) * QK_LD + cc0) = make_float2(y[0][r], y[1][r]);
+        } else {
+          const int i2 = item - NQK;
+          const int q = tq / 16, vc = 2 * (i2 % (G * D / 2));   // v channel within the group
+          const int hi = vc / D, dv0 = vc % D;
+          E* vb = reinterpret_cast<E*>(htile(hi, Gm::HV) - 16 * lane);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            E* dst = vb + (((dv0 >> 4) * 4 + q) * 64 + g4 * 16 + (dv0 & 15)) * 4;
+            if constexpr (BF16) {
+              *reinterpret_cast<uint4*>(dst) =
+                  make_uint4(pack2_bf16(y[0][4 * g4], y[0][4 * g4 + 1]), pack2_bf16(y[0][4 * g4 + 2], y[0][4 * g4 + 3]),
+                             pack2_bf16(y[1][4 * g4], y[1][4 * g4 + 1]), pack2_bf16(y[1][4 * g4 + 2], y[1][4 * g4 + 3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(y[0][4 * g4], y[0][4 * g4 + 1], y[0][4 * g4 + 2], y[0][4 * g4 + 3]);
+              *reinterpret_cast<float4*>(dst + 4) = make_float4(y[1][4 * g4], y[1][4 * g4 + 1], y[1][4 * g4 + 2], y[1][4 * g4 + 3]);
+            }
           }
         }
       }
