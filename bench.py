@@ -109,6 +109,12 @@ def parse():
                    help="run only the decode counter workload: the calibration copy, then four decode calls")
     p.add_argument("--pmc-summarize-decode", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the decode traffic summary from two rocprofv3 --pmc counter CSVs")
+    p.add_argument("--pmc-summarize-mfma", metavar="COUNTER_CSV",
+                   help="write the prefill MFMA-activity summary from a rocprofv3 --pmc counter CSV")
+    p.add_argument("--pmc-probe-verify", action="store_true",
+                   help="run only the verify counter workload: the calibration copy, then four verify calls")
+    p.add_argument("--pmc-summarize-verify", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the verify traffic summary from two rocprofv3 --pmc counter CSVs")
     return p.parse_args()
 
 
@@ -193,6 +199,132 @@ def pmc_probe_decode():
         gdn.decode_step(geom, pl, x, a, b, cw, sl, o)
         torch.cuda.synchronize()
     print("pmc decode probe done", flush=True)
+
+
+def pmc_probe_verify():
+    """Counter workload for verify: the calibration copy, then one 4-slot x
+    k = 4 verify on each of 4 slot pools (each call finds its state cold); the
+    last call is the one summarised."""
+    import torch
+    import gated_deltanet_delta_amd as gdn
+    import gdn_inputs as gi
+    gdn.lib()
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = gi.GEOM_QWEN
+    geom = gdn.Geometry()
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    vinp = gi.workload(5)
+    pools = []
+    for _ in range(4):
+        pl = gdn.SlotPool.zeros(geom)
+        pl.state.normal_(0.0, 0.02)
+        pools.append(pl)
+    x, a, b = (torch.from_numpy(vinp[k]).to(bf).to(dev) for k in ("x", "a", "b"))
+    cw = torch.from_numpy(vinp["conv_w"]).to(dev)
+    sl = torch.from_numpy(vinp["slots"]).to(dev)
+    snap = torch.empty(4, 4, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+    o = torch.empty(4, 4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+    torch.cuda.synchronize()
+    for pl in pools:
+        gdn.verify_k(geom, pl, x, a, b, cw, sl, snap, o)
+        torch.cuda.synchronize()
+    print("pmc verify probe done", flush=True)
+
+
+def pmc_summarize_verify(fetch_csv, write_csv):
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = pmc_read(path, counter)
+        calib = max((r for r in rows if "elementwise" in r[1]), key=lambda r: r[2])
+        last = [r for r in rows if "step_kernel" in r[1]][-1]
+        factor = CALIB_BYTES / (calib[2] * 1024.0)
+        out[counter] = (calib[2], factor, last[2] * 1024.0 * factor)
+    snap_bytes = 4 * 4 * 48 * 128 * 128 * 4
+    alg = {"FETCH_SIZE": VERIFY_BYTES - snap_bytes, "WRITE_SIZE": snap_bytes}
+    lines = ["# Verify HBM traffic, 4 slots x k = 4 drafts (16 k-heads, 48 v-heads, d = 128, bf16 inputs, "
+             "fp32 state)", "",
+             "Commands (from /tmp, TMPDIR=/tmp), one counter per run:", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d <dir_f> -o f --output-format csv -- python3 bench.py --pmc-probe-verify",
+             "    rocprofv3 --pmc WRITE_SIZE -d <dir_w> -o w --output-format csv -- python3 bench.py --pmc-probe-verify",
+             "    python3 bench.py --pmc-summarize-verify <dir_f>/f_counter_collection.csv "
+             "<dir_w>/w_counter_collection.csv", "",
+             "Scaled by the same %d-byte calibration copy as the prefill summary; the figures" % CALIB_BYTES,
+             "are the last of four verify calls, each on a slot pool of its own.", "",
+             "| counter | calibration copy (KiB) | scale | verify call (bytes) | algorithmic (bytes) |",
+             "|---|---|---|---|---|"]
+    for c, (kib, f, v) in out.items():
+        lines.append("| %s | %.0f | %.4f | %.0f | %d |" % (c, kib, f, v, alg[c]))
+    total = out["FETCH_SIZE"][2] + out["WRITE_SIZE"][2]
+    lines += ["", "The algorithmic write is the 16 snapshots (%d B); the algorithmic read is the" % snap_bytes,
+              "state (12 582 912 B), the conv history, x, a, b and the conv weights, with the outputs",
+              "and the drafts' ring rows counted there too (total %d B)." % VERIFY_BYTES, "",
+              "measured_total_bytes: %.0f" % total, "algorithmic_bytes: %d" % VERIFY_BYTES, ""]
+    path = os.path.join(ROOT, "profiles", "verify_traffic_4x4.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", path, "measured", int(total), "algorithmic", VERIFY_BYTES)
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def pmc_summarize_mfma(path):
+    """MFMA activity of the second prefill of --pmc-probe, from one counter run.
+    MFMA utilisation follows rocprofv3's own MfmaUtil expression (as listed by
+    rocprofv3 -L on the MI355X): 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) /
+    (max over XCDs of GRBM_GUI_ACTIVE * SIMD_NUM); the per-dispatch value of
+    GRBM_GUI_ACTIVE here is the sum over the 8 XCDs, so its max is taken as
+    that sum / 8.  Executed flops: MOPS x 512."""
+    import csv
+    agg, names = {}, {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            d = int(r["Dispatch_Id"])
+            agg.setdefault(d, {}).setdefault(r["Counter_Name"], 0.0)
+            agg[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"].split("(")[0]
+            agg[d]["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    disp = [d for d in sorted(agg) if "prefill_kernel" in names[d]][-1]
+    v = agg[disp]
+    active = v["GRBM_GUI_ACTIVE"] / N_XCD
+    util = 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * N_SIMD)
+    fl_bf16 = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    fl_f32 = v["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512
+    ns = v["_ns"]
+    alg = PREFILL_FLOP_PER_TOKEN * T_PREFILL
+    lines = ["# Prefill MFMA activity, T = 8192 (16 k-heads, 48 v-heads, d = 128, bf16)", "",
+             "Command (from /tmp, TMPDIR=/tmp), one counter run:", "",
+             "    rocprofv3 --pmc %s -d <dir> -o m --output-format csv -- python3 bench.py --pmc-probe"
+             % " ".join(MFMA_COUNTERS),
+             "    python3 bench.py --pmc-summarize-mfma <dir>/m_counter_collection.csv", "",
+             "The counter names were taken from `rocprofv3 -L` on the MI355X, whose derived",
+             "metric MfmaUtil is 100 * reduce(SQ_VALU_MFMA_BUSY_CYCLES, sum) /",
+             "(reduce(GRBM_GUI_ACTIVE, max) * SIMD_NUM).  The dispatch summarised is the",
+             "prefill kernel of the second of the probe's two prefills (`%s`)." % names[disp], "",
+             "| counter | value |", "|---|---|"]
+    for c in MFMA_COUNTERS:
+        lines.append("| %s | %.0f |" % (c, v[c]))
+    lines += ["", "| figure | value |", "|---|---|",
+              "| dispatch duration (counter run, serialised) | %.1f us |" % (ns / 1e3),
+              "| GPU-active cycles per XCD | %.0f |" % active,
+              "| MFMA utilisation (MfmaUtil) | %.2f %% |" % util,
+              "| bf16 MFMA flops executed (MOPS x 512) | %.3e |" % fl_bf16,
+              "| fp32 MFMA flops executed (MOPS x 512) | %.3e |" % fl_f32,
+              "| algorithmic flops (%d per token x %d) | %.3e |" % (PREFILL_FLOP_PER_TOKEN, T_PREFILL, alg),
+              "| executed bf16 flops / (duration x 2.5 PFLOP/s) | %.2f %% |" % (100.0 * fl_bf16 / (ns * 1e-9) / 2.5e15),
+              "", "mfma_util_pct: %.2f" % util, "source_sha256: %s" % prefill_source_hash(), ""]
+    path_out = os.path.join(ROOT, "profiles", "prefill_mfma_T8192.md")
+    with open(path_out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", path_out, "mfma util %.2f %%" % util)
 
 
 def pmc_summarize_decode(fetch_csv, write_csv):
@@ -299,6 +431,12 @@ def main():
     if args.pmc_summarize_decode:
         pmc_summarize_decode(*args.pmc_summarize_decode)
         return
+    if args.pmc_summarize_verify:
+        pmc_summarize_verify(*args.pmc_summarize_verify)
+        return
+    if args.pmc_summarize_mfma:
+        pmc_summarize_mfma(args.pmc_summarize_mfma)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the layer's multi-GPU "
                                    "sharding is a design note, not a measured path", "n_gpus": args.gpus}))
@@ -315,6 +453,9 @@ def main():
         return
     if args.pmc_probe_decode:
         pmc_probe_decode()
+        return
+    if args.pmc_probe_verify:
+        pmc_probe_verify()
         return
     gdn.lib()
     dev = torch.device("cuda:0")
@@ -714,7 +855,7 @@ def main():
                    "n_k_heads": 16, "n_v_heads": 48, "d_k": 128, "d_v": 128, "conv_width": 4,
                    "chunk": 64, "seq_len": T_PREFILL, "decode_slots": 4, "verify_k": 4,
                    "state_dtype": "f32", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "gdn_prefill_chunked (plan + chunk + state kernels)",
+        "roofline": {"bound": "mfma", "kernel": "gdn_prefill_chunked (one call: plan_kernel + prefill_kernel)",
                      "achieved": round(prefill_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic()},
         "prefill": {"ms": round(ms_prefill, 4), "tokens_per_s": round(T_PREFILL / (ms_prefill * 1e-3), 1),
@@ -738,27 +879,106 @@ def main():
         "wall_s": round(wall, 3),
     }
 
-    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
-    # (the only place the benchmark touches the oracle; its outputs double as a
-    # parity check of the GPU prefill on the same tokens)
+    # ---------------- CPU baseline and parity: the oracle ----------------
+    # (the only place the benchmark touches the oracle).  Two timings of the
+    # unchanged fp64 oracle on this host:
+    #   all cores: the whole T = 8192 sequence, all 48 v-heads, the 16 k-head
+    #     groups as independent sub-problems over a pool of worker processes
+    #     (at most 16); its output is also the parity gate of the GPU prefill
+    #     on every token and head;
+    #   one core: the first --cpu-tokens tokens, all heads, in this process.
+    # Then one decode call and one verify call of the GPU, each on a copy of a
+    # benchmark slot pool, against the oracle from the same states.
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import gdn_oracle as orc
+        from oracle import groups as og
+
+        def relmax(got, ref):
+            return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+        def gate(name, err_val, tol=2e-2):
+            if not (np.isfinite(err_val) and err_val <= tol):
+                print(json.dumps({"error": f"{name} parity vs oracle failed: rel err {err_val:.3e}"}))
+                sys.exit(4)
+
+        with og.make_pool() as ex:
+            n_workers = ex._max_workers
+            list(ex.map(og.ping, range(4 * n_workers)))  # workers started before the clock
+            c0 = time.perf_counter()
+            o_all, _, heads = og.prefill_by_groups(g, pin, executor=ex)
+            cs_all = time.perf_counter() - c0
+        got_all = po.float().cpu().numpy()[:, heads]
+        parity_full = relmax(got_all, o_all)
+        gate("prefill (all tokens, all heads)", parity_full)
+
         n = args.cpu_tokens
         with threadpool_limits(1):
             c0 = time.perf_counter()
             o_ref, _, _ = orc.layer_sequence(g, pin["x"][:n], pin["a"][:n], pin["b"][:n], pin["conv_w"],
                                              np.zeros((g.n_v_heads, 128, 128)), np.zeros((3, g.conv_channels)))
             cs = time.perf_counter() - c0
-        got = po[:n].float().cpu().numpy()
-        parity = float(np.max(np.abs(got - o_ref)) / np.max(np.abs(o_ref)))
-        if not parity <= 2e-2:
-            print(json.dumps({"error": f"prefill parity vs oracle failed: rel err {parity:.3e}"}))
-            sys.exit(4)
-        out["prefill"]["parity_rel_err_vs_oracle"] = parity
-        out["cpu_baseline"] = {"value": round(n / cs, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"fp64 oracle, first {n} tokens of the T=8192 prefill, all 48 v-heads, "
-                                         f"{cs:.1f} s on one host core"}
+        parity = relmax(po[:n].float().cpu().numpy(), o_ref)
+        gate("prefill (prefix)", parity)
+
+        # decode and verify from copies of two benchmark pools (random states and
+        # conv rings, position 0: the history is ring rows 5, 6, 7)
+        def host_pool(pl):
+            st = pl.state.cpu().numpy().astype(np.float64)
+            ring = pl.conv_state.cpu().numpy()
+            pos = (pl.conv_pos[:, 0].cpu().numpy().astype(np.int64) & 0xFFFFFFFF) >> 16
+            hist = np.stack([np.stack([ring[s, (int(pos[s]) - 3 + i) % g.conv_ring] for i in range(3)])
+                             for s in range(g.n_slots)]).astype(np.float64)
+            return st, hist
+
+        def copy_pool(pl):
+            return gdn.SlotPool(pl.state.clone(), pl.conv_state.clone(), pl.conv_pos.clone())
+
+        cp = copy_pool(pools[0])
+        st0, hi0 = host_pool(cp)
+        o_chk = torch.empty(4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+        gdn.decode_step(geom, cp, dx, da, db, cw, dslot, o_chk, dev_err=err)
+        torch.cuda.synchronize()
+        o_d, st_d, _ = orc.decode_step(g, st0, hi0, dinp["x"][:, 0], dinp["a"][:, 0], dinp["b"][:, 0],
+                                       pin["conv_w"], dinp["slots"])
+        sl_d = [int(s) for s in dinp["slots"]]
+        parity_decode = max(relmax(o_chk.float().cpu().numpy(), o_d),
+                            relmax(cp.state.cpu().numpy()[sl_d], st_d[sl_d]))
+        gate("decode", parity_decode)
+        cp = copy_pool(pools[1])
+        st1, hi1 = host_pool(cp)
+        vo_chk = torch.empty(4, 4, g.n_v_heads, g.d_v, dtype=bf, device=dev)
+        snap_chk = torch.empty(4, 4, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device=dev)
+        gdn.verify_k(geom, cp, vx, va, vb, cw, vslot, snap_chk, vo_chk, dev_err=err)
+        torch.cuda.synchronize()
+        parity_verify = 0.0
+        for i, s_ in enumerate(vinp["slots"]):
+            o_v, snaps_v, _ = orc.verify(g, st1[int(s_)], hi1[int(s_)], vinp["x"][i], vinp["a"][i], vinp["b"][i],
+                                         pin["conv_w"])
+            parity_verify = max(parity_verify, relmax(vo_chk[i].float().cpu().numpy(), o_v),
+                                relmax(snap_chk[i].cpu().numpy(), snaps_v))
+        gate("verify", parity_verify)
+        if int(err.item()) != 0:
+            print(json.dumps({"error": f"device error code {int(err.item())} in the parity calls"}))
+            sys.exit(3)
+
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
+        out["prefill"]["parity_rel_err_vs_oracle"] = parity_full
+        out["prefill"]["parity_rel_err_vs_oracle_prefix"] = parity
+        out["decode"]["parity_rel_err_vs_oracle"] = parity_decode
+        out["verify"]["parity_rel_err_vs_oracle"] = parity_verify
+        out["cpu_baseline"] = {
+            "value": round(T_PREFILL / cs_all, 2), "unit": "tokens/s", "cores": n_workers, "kind": "oracle",
+            "sample": f"fp64 oracle, the whole T=8192 prefill, all 48 v-heads, the 16 k-head groups over "
+                      f"{n_workers} worker processes (one thread each), {cs_all:.1f} s wall",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
+            "single_core": {"value": round(n / cs, 2), "unit": "tokens/s", "cores": 1,
+                            "sample": f"first {n} tokens, all 48 v-heads, {cs:.1f} s on one core"}}
     print(json.dumps(out))
 
 

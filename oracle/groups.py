@@ -9,10 +9,11 @@ kh, k of kh and v of those heads, in that order, with the matching columns of
 the gate inputs and slices of the state and conv history.  Each worker runs
 the unchanged oracle on such a sub-problem; the parent puts the pieces back.
 
-Test infrastructure only.  The workers import numpy and the oracle, nothing
-that touches a GPU; they are started with the "spawn" method (a fresh
-interpreter, no copy of a process that holds a GPU context), one BLAS thread
-each, at most 16 of them.
+Test infrastructure, like the oracle itself: only the tests and the
+benchmark's CPU-baseline leg use it.  The workers import numpy and the
+oracle, nothing that touches a GPU; they are started with the "spawn" method
+(a fresh interpreter, no copy of a process that holds a GPU context), one
+BLAS thread each, at most 16 of them.
 """
 from __future__ import annotations
 
@@ -36,7 +37,12 @@ def _geometry(fields: dict):
     return g
 
 
-def _init_worker():
+def ping(_):
+    """A no-op job: mapping it over the pool starts the workers."""
+    return os.getpid()
+
+
+def init_worker():
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)
@@ -50,6 +56,12 @@ def _run(job):
     return orc.prefill(_geometry(fields), x, a, b, conv_w, cu, S0, h0, has_init)
 
 
+def make_pool(workers=None) -> ProcessPoolExecutor:
+    """A pool of spawned oracle workers: at most 16, at most the host's CPUs."""
+    n = max(1, min(MAX_WORKERS, workers or MAX_WORKERS, os.cpu_count() or 1))
+    return ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=init_worker)
+
+
 def channels(g, kh: int, heads) -> np.ndarray:
     """Channel indices of the sub-problem of k-head kh with v-heads ``heads``."""
     D, Hk = g.d_k, g.n_k_heads
@@ -58,14 +70,15 @@ def channels(g, kh: int, heads) -> np.ndarray:
     return np.concatenate(parts)
 
 
-def prefill_by_groups(g, inp, heads_of_group=None, workers=None):
+def prefill_by_groups(g, inp, heads_of_group=None, workers=None, executor=None):
     """orc.prefill on ``inp`` (a prefill_inputs dict) for the v-heads chosen per
     k-head group (all of them by default), computed per group in parallel.
 
     heads_of_group(kh) -> list of v-heads of group kh.  Returns (o, finals, heads)
     with o (N, len(heads), d_v), finals[s] = (S_T (len(heads), d_v, d_k),
     hist_T (W-1, C) with the channels no chosen head reads left as NaN) and
-    heads the v-heads in the order of o's second axis.
+    heads the v-heads in the order of o's second axis.  ``executor``: a
+    running process pool to use (one is made and shut down otherwise).
     """
     G = g.n_v_heads // g.n_k_heads
     pick = heads_of_group or (lambda kh: list(range(kh * G, (kh + 1) * G)))
@@ -84,9 +97,11 @@ def prefill_by_groups(g, inp, heads_of_group=None, workers=None):
                      inp["cu_seqlens"], np.ascontiguousarray(S0[:, hs]), np.ascontiguousarray(h0[:, :, ch]),
                      inp["has_init"]))
         layout.append((hs, ch))
-    n = min(MAX_WORKERS, workers or MAX_WORKERS, len(jobs), os.cpu_count() or 1)
-    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=_init_worker) as ex:
-        results = list(ex.map(_run, jobs))
+    if executor is not None:
+        results = list(executor.map(_run, jobs))
+    else:
+        with make_pool(min(len(jobs), workers or MAX_WORKERS)) as ex:
+            results = list(ex.map(_run, jobs))
     heads = [h for hs, _ in layout for h in hs]
     N = inp["x"].shape[0]
     o = np.empty((N, len(heads), g.d_v))

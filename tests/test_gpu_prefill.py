@@ -7,8 +7,8 @@ import torch
 
 import gdn_inputs as gi
 import harness as H
-import oracle_groups as OG
 from oracle import gdn_oracle as orc
+from oracle import groups as OG
 
 pytestmark = pytest.mark.gpu
 

@@ -5,8 +5,8 @@ import dataclasses
 import numpy as np
 
 import gdn_inputs as gi
-import oracle_groups as OG
 from oracle import gdn_oracle as orc
+from oracle import groups as OG
 
 
 def _whole(g, inp, heads=None):
