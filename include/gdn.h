@@ -125,7 +125,7 @@ typedef struct gdn_geometry {
   int32_t n_v_heads;      /* H_v, a multiple of H_k */
   int32_t d_k;            /* state columns (ssm_state_size) */
   int32_t d_v;            /* state rows; the library requires d_v == d_k in {16,32,64,128} */
-  int32_t conv_width;     /* W in {0,2,3,4}; 0 = no conv and no SiLU: x holds q | k | v */
+  int32_t conv_width;     /* W in 0..4 (this library: 0 or 4); 0 = no conv and no SiLU: x holds q | k | v */
   int32_t conv_channels;  /* C, must equal 2*H_k*d_k + H_v*d_v */
   int32_t conv_ring;      /* R, power of two >= W-1+max_draft (ignored when W = 0) */
   int32_t max_draft;      /* largest k accepted by gdn_verify_k (1..16) */
@@ -155,6 +155,9 @@ int32_t gdn_abi_version(void);
  * with a message (also copied into msg when msg != NULL, NUL-terminated,
  * truncated to msg_len) naming the field, the value found and the value
  * required.  GDN_ERR_UNSUPPORTED means consistent but not built here.
+ * ("Chapter 6: engine startup and memory plan", section 6.2: the layer's
+ * geometry is checked once at start-up, and a refusal states the field, the
+ * value found and the value required.)
  */
 gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len);
 
@@ -169,6 +172,18 @@ gdn_status gdn_check_geometry(const gdn_geometry* g, char* msg, size_t msg_len);
  */
 size_t gdn_prefill_workspace_bytes(const gdn_geometry* g, int32_t n_tokens, int32_t n_seqs);
 
+/*
+ * The conv front end alone, one token per batch row: for every one of the C
+ * channels, y = SiLU(causal depthwise conv over the slot's last W-1 inputs
+ * and x) (taps oldest first, conv_w [C][W] fp32), then x is appended to the
+ * slot's ring and conv_pos advances one token.  No norm, gates or state.
+ *   x [batch][C] (dtype_in), y [batch][C] (dtype_out), slot [batch] int32.
+ *   1 <= batch <= n_slots; requires conv_width = 4.
+ * ("Hybrid transformers under load", section 3: the short causal
+ * convolution ahead of the delta rule, whose state between tokens is the last
+ * W-1 inputs; "Chapter 6: engine startup and memory plan", section 6.2:
+ * ssm_d_conv = 4 over ssm_conv_channels = 10240.)
+ */
 gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t* conv_pos,
                                const void* x, const float* conv_w, const int32_t* slot,
                                int32_t batch, void* y, int32_t* dev_err, void* stream);
@@ -176,7 +191,10 @@ gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t
 /*
  * One decode token per batch row, fused: conv ring + SiLU, L2 norm of q and k,
  * gates, the delta-rule update of the slot's state in place, and the output.
- * Each fp32 state row is read once and written once.
+ * Each fp32 state row is read once and written once ("Hybrid transformers
+ * under load", section 3: the gated delta rule, one token at a time against
+ * a fixed-size state; "Forge", section on the formulas that decide
+ * everything: a decode step costs the bytes it moves over the bandwidth).
  *   x [batch][C], a, b [batch][H_v] (dtype_in); o [batch][H_v][d_v] (dtype_out);
  *   slot [batch] int32 (device).  Advances conv_pos of each slot by one token.
  *   1 <= batch <= n_slots.
@@ -297,6 +315,10 @@ gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_s
  * for each batch row with n = accepted[i] (device int32 [batch], 0..k):
  * if n >= 1 the slot's state becomes a bitwise copy of snap[i][n-1] and
  * conv_pos advances n tokens; n = 0 leaves the slot unchanged.
+ * ("Forge", 27 August: with a snapshot after every draft row, rolling the
+ * recurrent state back to the last accepted draft is a copy, not a replay.)
+ * An accepted length out of range sets GDN_DEV_BAD_ACCEPTED and the row is
+ * skipped.
  */
 gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos,
                         const float* snap, const int32_t* slot, const int32_t* accepted,
@@ -339,7 +361,8 @@ gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_s
  * other slots of the row (slot[i] when n >= 1, and the snapshot slots not
  * chosen) hold nothing the sequence needs any more.  An accepted length out
  * of range sets GDN_DEV_BAD_ACCEPTED (a draft count out of range,
- * GDN_DEV_BAD_K) and keeps slot[i].
+ * GDN_DEV_BAD_K) and keeps slot[i].  ("Forge", 27 August: the accepted
+ * draft's snapshot becomes the state the sequence continues from.)
  */
 gdn_status gdn_commit_slots(const gdn_geometry* g, const int32_t* slot, const int32_t* k_row,
                             const int32_t* snap_slot, const int32_t* accepted, int32_t batch, int32_t k,
