@@ -105,7 +105,7 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int Hk, int Hv, int D, bool bf16, int n_tokens, int n_seqs);
 int prefill_max_chunks(int n_tokens, int n_seqs);
-int prefill_launches(int Hk, int Hv);
+int prefill_launches(int Hk, int Hv, int D, bool bf16);
 constexpr int kChunk = 64;
 
 // Launchers: return 0 on success, else the hipError_t value.

@@ -115,7 +115,15 @@ struct TriTiles {
   }
 };
 
+// A v-head's chain runs as NCG workgroups, each owning NT / NCG 16-row tiles
+// of d_v (the columns of S^T): every product of the chain splits along d_v
+// with no exchange between them.  The plain prefill uses one workgroup per
+// head; the prefill with checkpoints, whose chain keeps more values live,
+// uses two at d = 128 (bf16), so that a compute wave holds one tile.
 template <int D, bool BF16>
+constexpr int ncg_ckpt() { return (D == 128 && BF16) ? 2 : 1; }
+
+template <int D, bool BF16, int NCG_ = 1>
 struct Geo {
   using P = Pk<BF16>;
   static constexpr int KSD = (D + P::SK - 1) / P::SK;  // packed tiles along d
@@ -135,14 +143,18 @@ struct Geo {
   static constexpr int HT = 0, HP = NTRI, HG = 2 * NTRI, HV = 2 * NTRI + 1, HEAD_TILES = HV + NV;
   // gate tile: e^G [64], e^{G_last - G} [64], G [64], e^{G_last} (64 copies)
   static constexpr int G_EG = 0, G_D = 64, G_G = 128, G_EGL = 192;
-  // A chain stage in LDS: the item's shared tiles, then one head's tiles
-  static constexpr int STAGE_TILES = HEAD0 + HEAD_TILES;
+  static constexpr int NCG = NCG_;
+  static constexpr int NTG = NT / NCG;                 // d_v tiles of one chain workgroup
+  static constexpr int NVG = NV / NCG;                 // its V tiles (contiguous: tile-major in d_v)
+  // A chain stage in LDS: the item's shared tiles, then one head's T, P and
+  // gate tiles, then the workgroup's V tiles
+  static constexpr int STAGE_TILES = HEAD0 + HV + NVG;
   static constexpr size_t V_OFF = static_cast<size_t>(HEAD0 + HV) * kTileBytes;
   static constexpr size_t STAGE_BYTES = static_cast<size_t>(STAGE_TILES) * kTileBytes;
   static constexpr int NBUF = 2 * STAGE_BYTES <= kLdsStageMax ? 2 : 1;
   // chain compute waves: CT 16-row tiles of d_v each
-  static constexpr int CT = NT >= 2 ? 2 : 1;
-  static constexpr int NWC = NT / CT;
+  static constexpr int CT = NCG > 1 ? 1 : (NT >= 2 ? 2 : 1);
+  static constexpr int NWC = NTG / CT;
   static size_t item_bytes(int G) { return static_cast<size_t>(HEAD0 + G * HEAD_TILES) * kTileBytes; }
 };
 
@@ -153,16 +165,20 @@ int prefill_max_chunks(int n_tokens, int n_seqs) {
 }
 
 // k-heads of one launch: 8 XCDs x as many k-heads per XCD as keep the chain
-// workgroups of an XCD within kMaxChainPerXcd.
-static int heads_per_launch(int Hk, int Hv) {
-  const int G = Hv / Hk;
-  const int per_xcd = kMaxChainPerXcd / G > 0 ? kMaxChainPerXcd / G : 1;
+// workgroups of an XCD (G x NCG per k-head) within kMaxChainPerXcd.
+static int heads_per_launch(int Hk, int Hv, int ncg) {
+  const int per_head = (Hv / Hk) * ncg;
+  const int per_xcd = kMaxChainPerXcd / per_head > 0 ? kMaxChainPerXcd / per_head : 1;
   return kXcd * per_xcd;
 }
 
-int prefill_launches(int Hk, int Hv) {
-  const int n = heads_per_launch(Hk, Hv);
+static int launches(int Hk, int Hv, int ncg) {
+  const int n = heads_per_launch(Hk, Hv, ncg);
   return (Hk + n - 1) / n;
+}
+
+int prefill_launches(int Hk, int Hv, int D, bool bf16) {
+  return launches(Hk, Hv, (D == 128 && bf16) ? 2 : 1);  // the larger of the two variants' counts
 }
 
 template <int D, bool BF16>
@@ -178,8 +194,9 @@ static PrefillLayout layout_t(int Hk, int Hv, int n_tokens, int S) {
   L.hdr = take(2 * kLine * 4);
   L.seq_tab = take(static_cast<size_t>(S) * 8 * 4);
   L.ready = take(static_cast<size_t>(L.ring_slots) * Hk * kLine * 4);
-  L.consumed = take(static_cast<size_t>(Hv) * kLine * 4);
-  L.ctr = take(static_cast<size_t>(prefill_launches(Hk, Hv)) * kCtrLines * kLine * 4);
+  // sized for the variant with more chains (the one with checkpoints)
+  L.consumed = take(static_cast<size_t>(Hv) * ncg_ckpt<D, BF16>() * kLine * 4);
+  L.ctr = take(static_cast<size_t>(launches(Hk, Hv, ncg_ckpt<D, BF16>())) * kCtrLines * kLine * 4);
   L.total = off;
   return L;
 }
@@ -301,7 +318,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs A, PrefillLayout 
   int32_t* ready = ws_ptr<int32_t>(A.workspace, L.ready);
   for (int i = threadIdx.x; i < L.ring_slots * A.Hk; i += blockDim.x) ready[i * kLine] = 0;
   int32_t* consumed = ws_ptr<int32_t>(A.workspace, L.consumed);
-  for (int i = threadIdx.x; i < A.Hv; i += blockDim.x) consumed[i * kLine] = 0;
+  const int n_cons = static_cast<int>((L.ctr - L.consumed) / (kLine * 4));  // every chain's line
+  for (int i = threadIdx.x; i < n_cons; i += blockDim.x) consumed[i * kLine] = 0;
   int32_t* ctr = ws_ptr<int32_t>(A.workspace, L.ctr);
   for (int i = threadIdx.x; i < n_launch * kCtrLines * kLine; i += blockDim.x) ctr[i] = 0;
 }
@@ -612,15 +630,15 @@ struct ProdSmem {
   static constexpr size_t BYTES = R0 + R1 + AM + MISC;
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, int NCG>
 struct SmemBytes {
   static constexpr size_t P = ProdSmem<D, BF16>::BYTES;
-  static constexpr size_t Ch = Geo<D, BF16>::NBUF * Geo<D, BF16>::STAGE_BYTES;
+  static constexpr size_t Ch = Geo<D, BF16, NCG>::NBUF * Geo<D, BF16, NCG>::STAGE_BYTES;
   static constexpr size_t value = P > Ch ? P : Ch;
   static_assert(value <= 158 * 1024, "LDS plan exceeds the CU's LDS");
 };
 
-template <int D, bool BF16, int KW>
+template <int D, bool BF16, int KW, int NCG>
 __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int chunk, int kh) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
@@ -667,8 +685,9 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   if (chunk >= RS) {
     if (tid == 0) {
       const int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
-      for (int hh = 0; hh < G; ++hh)
-        if (!wait_at_least(consumed + (kh * G + hh) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err)) break;
+      for (int hh = 0; hh < G * NCG; ++hh)
+        if (!wait_at_least(consumed + (kh * G * NCG + hh) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err))
+          break;
     }
     lds_barrier();
   }
@@ -988,21 +1007,23 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
 // ---------------------------------------------------------------------------
 // chain: one workgroup per v-head walks every sequence's chunks in order
 // ---------------------------------------------------------------------------
-// Waves 0 .. NWC-1 compute: wave w holds the 16-row tiles CT w .. CT w + CT-1
-// of d_v, i.e. columns of S^T, as NT accumulator tiles each.  Waves NWC .. 7
-// are helpers: for chunk c+1 while the compute waves work on chunk c, they
-// wait for the producer's flag and copy the item's operand tiles from the L2
-// into LDS.  One workgroup barrier per chunk swaps the two LDS buffers (two
-// barriers when the geometry leaves room for one buffer).
-template <int D, bool BF16, int KW, bool CKPT>
-__device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int kh, int h) {
+// The chain of v-head h runs as NCG workgroups; workgroup cg owns the d_v
+// tiles cg NTG .. cg NTG + NTG-1.  Its waves 0 .. NWC-1 compute: wave w holds
+// the 16-row tiles cg NTG + CT w .. + CT-1 of d_v, i.e. columns of S^T, as NT
+// accumulator tiles each.  Waves NWC .. 7 are helpers: for chunk c+1 while
+// the compute waves work on chunk c, they wait for the producer's flag and
+// copy the item's operand tiles from the L2 into LDS.  One workgroup barrier
+// per chunk swaps the two LDS buffers (two barriers when the geometry leaves
+// room for one buffer).
+template <int D, bool BF16, int KW, bool CKPT, int NCG>
+__device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int kh, int h, int cg) {
   using P = Pk<BF16>;
-  using Gm = Geo<D, BF16>;
+  using Gm = Geo<D, BF16, NCG>;
   using Ch = Chain<BF16>;
   using E = typename P::E;
   using Bop = typename Ch::Bop;
   constexpr int KSD = Gm::KSD, KSC = Gm::KSC, NT = Gm::NT, TPS = Gm::TPS, SK = P::SK;
-  constexpr int CT = Gm::CT, NWC = Gm::NWC, NBUF = Gm::NBUF, NTRI = Gm::NTRI;
+  constexpr int CT = Gm::CT, NWC = Gm::NWC, NBUF = Gm::NBUF, NTRI = Gm::NTRI, NTG = Gm::NTG;
   constexpr int NHW = kWaves - NWC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -1051,7 +1072,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       return ov;
     };
     auto write_out = [&](int tok0, int clen, const Pieces& ov) {
-      E* og = static_cast<E*>(A.o) + static_cast<size_t>(tok0) * rowstride + h * D;
+      E* og = static_cast<E*>(A.o) + static_cast<size_t>(tok0) * rowstride + h * D + cg * NTG * 16;
 #pragma unroll
       for (int q = 0; q < NVP; ++q) {
         const int t = vt_first + NHW * q;
@@ -1070,7 +1091,8 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 #pragma unroll
       for (int j = 0; j < NCP; ++j) {
         const int t = hw + j * NHW;
-        const int src = t < Gm::HEAD0 ? t : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0);
+        const int src = t < Gm::HEAD0 ? t
+                                      : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0) + (t >= VT0 ? cg * Gm::NVG : 0);
         if (t < Gm::STAGE_TILES) load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane), b + static_cast<size_t>(t) * kTileBytes);
       }
     };
@@ -1099,7 +1121,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       wait_vm();   // this wave's loads of chunk c are in LDS
       lds_sync();  // chunk c staged
       if (hw == 0 && lane == 0)
-        __hip_atomic_store(consumed + h * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(consumed + (h * NCG + cg) * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (NBUF == 2) {
         const Pieces ov = read_out(c - 1 < 0 ? 0 : c - 1);
         if (c + 1 < total) fill(c + 1);
@@ -1122,7 +1144,8 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
   }
 
   // ================= compute waves =================
-  const int dvt0 = wave * CT;  // first 16-row tile of d_v
+  const int wl0 = wave * CT;       // first d_v tile of this wave within the workgroup's (V region, O slice)
+  const int dvt0 = cg * NTG + wl0;  // first 16-row tile of d_v
   const size_t rowstride = static_cast<size_t>(Hv) * D;
   int c = 0;
   for (int s = 0; s < S; ++s) {
@@ -1241,7 +1264,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((dvt0 + ct) * 4 + mt) * 64 + lane) * 4);
+          vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((wl0 + ct) * 4 + mt) * 64 + lane) * 4);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) egv[mt] = gvec(Gm::G_EG, mt);
       times_S(qa, O, std::true_type{});
@@ -1344,7 +1367,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       // so that no store of this wave has to complete before its registers
       // are reused.
       auto write_o = [&] {
-        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + dvt0 * 4 * 256;
+        E* ol = reinterpret_cast<E*>(const_cast<char*>(base) + Gm::V_OFF) + wl0 * 4 * 256;
         constexpr int RW = CT * 16;                // d_v of a token row in this slice
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -1425,8 +1448,9 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 
     // ---- final state back to the slot ----
     store_state(Sg, st);
-    // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1 ----
-    if (A.W > 0) {
+    // ---- conv history: the last W-1 inputs go to ring rows pos_end-1 .. pos_end-W+1
+    // (by the first column group of each head) ----
+    if (A.W > 0 && cg == 0) {
       const int W = A.W, R = A.R;
       const uint32_t pos_end = (init ? pos0 : 0u) + static_cast<uint32_t>(len);
       float* ring = A.conv_state + static_cast<size_t>(slot) * R * C;
@@ -1455,7 +1479,8 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 // values live; the plain prefill does not carry them).
 template <int D, bool BF16, int KW, bool CKPT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, PrefillLayout L) {
-  __shared__ __attribute__((aligned(1024))) char smem[SmemBytes<D, BF16>::value];
+  constexpr int NCG = CKPT ? ncg_ckpt<D, BF16>() : 1;
+  __shared__ __attribute__((aligned(1024))) char smem[SmemBytes<D, BF16, NCG>::value];
   __shared__ int s_tk[2];
   const int tid = threadIdx.x;
   const int G = A.Hv / A.Hk;
@@ -1470,12 +1495,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
   // k-heads of this XCD in this launch: kh_lo + xcc + 8 j
   const int span = A.kh_hi - A.kh_lo;
   const int nk = span > xcc ? (span - xcc + kXcd - 1) / kXcd : 0;
-  const int n_chain = nk * G;
+  const int n_chain = nk * G * NCG;  // chains of this XCD: (k-head, v-head, column group)
   const int total = ws_ptr<int32_t>(A.workspace, L.hdr)[HDR_TOTAL];
   int chain_done = 0, items_done = 0;
   if (ticket < n_chain) {
-    const int kh = A.kh_lo + xcc + kXcd * (ticket / G);
-    chain_role<D, BF16, KW, CKPT>(A, L, smem, kh, kh * G + ticket % G);
+    const int kh = A.kh_lo + xcc + kXcd * (ticket / (G * NCG));
+    const int r = ticket % (G * NCG);
+    chain_role<D, BF16, KW, CKPT, NCG>(A, L, smem, kh, kh * G + r / NCG, r % NCG);
     chain_done = 1;
   } else if (nk > 0) {
     const int n_items = total * nk;
@@ -1485,7 +1511,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
       __syncthreads();
       const int it = s_tk[1];
       if (it >= n_items) break;
-      produce<D, BF16, KW>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk));
+      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk));
       ++items_done;
     }
   }
@@ -1498,7 +1524,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
         atomicAdd(reinterpret_cast<unsigned long long*>(ctr + 2 * kXcd * kLine), add);
     if ((old >> 48) == gridDim.x - 1) {
       const unsigned long long all = old + add;
-      const unsigned long long want_chain = static_cast<unsigned long long>(span) * G;
+      const unsigned long long want_chain = static_cast<unsigned long long>(span) * G * NCG;
       const unsigned long long want_items = static_cast<unsigned long long>(total) * span;
       if (((all >> 32) & 0xffffull) != want_chain || (all & 0xffffffffull) != want_items)
         report_error(A.dev_err, GDN_DEV_INCOMPLETE);
@@ -1512,8 +1538,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
 template <int D, bool BF16>
 static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st) {
   const PrefillLayout L = layout_t<D, BF16>(a0.Hk, a0.Hv, a0.n_tokens, a0.n_seqs);
-  const int n_launch = prefill_launches(a0.Hk, a0.Hv);
-  const int per = heads_per_launch(a0.Hk, a0.Hv);
+  const int ncg = a0.ckpt_every > 0 ? ncg_ckpt<D, BF16>() : 1;  // as the kernel variant chosen below
+  const int n_launch = launches(a0.Hk, a0.Hv, ncg);
+  const int per = heads_per_launch(a0.Hk, a0.Hv, ncg);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L, n_launch);
   int e = static_cast<int>(hipGetLastError());
   if (e) return e;
