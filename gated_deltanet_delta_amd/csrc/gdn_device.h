@@ -174,6 +174,11 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 __device__ __forceinline__ f32x4_t load4(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
+// Makes x opaque to the compiler at this point: the reads that produced it
+// are complete here and cannot be moved into a later conditional block, where
+// each would be waited for on its own.
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+
 // 16-byte non-temporal load: data read once, not kept in the caches.
 __device__ __forceinline__ f32x4_t load_nt4(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));

@@ -117,11 +117,11 @@ struct TriTiles {
 
 // A v-head's chain runs as NCG workgroups, each owning NT / NCG 16-row tiles
 // of d_v (the columns of S^T): every product of the chain splits along d_v
-// with no exchange between them.  The plain prefill uses one workgroup per
-// head; the prefill with checkpoints, whose chain keeps more values live,
-// uses two at d = 128 (bf16), so that a compute wave holds one tile.
+// with no exchange between them.  At d = 128 (bf16) there are two, so that a
+// compute wave holds one tile: its chunk step is shorter, and the chain with
+// checkpoints fits the registers.
 template <int D, bool BF16>
-constexpr int ncg_ckpt() { return (D == 128 && BF16) ? 2 : 1; }
+constexpr int ncg_of() { return (D == 128 && BF16) ? 2 : 1; }
 
 template <int D, bool BF16, int NCG_ = 1>
 struct Geo {
@@ -178,7 +178,7 @@ static int launches(int Hk, int Hv, int ncg) {
 }
 
 int prefill_launches(int Hk, int Hv, int D, bool bf16) {
-  return launches(Hk, Hv, (D == 128 && bf16) ? 2 : 1);  // the larger of the two variants' counts
+  return launches(Hk, Hv, (D == 128 && bf16) ? ncg_of<128, true>() : 1);
 }
 
 template <int D, bool BF16>
@@ -194,9 +194,8 @@ static PrefillLayout layout_t(int Hk, int Hv, int n_tokens, int S) {
   L.hdr = take(2 * kLine * 4);
   L.seq_tab = take(static_cast<size_t>(S) * 8 * 4);
   L.ready = take(static_cast<size_t>(L.ring_slots) * Hk * kLine * 4);
-  // sized for the variant with more chains (the one with checkpoints)
-  L.consumed = take(static_cast<size_t>(Hv) * ncg_ckpt<D, BF16>() * kLine * 4);
-  L.ctr = take(static_cast<size_t>(launches(Hk, Hv, ncg_ckpt<D, BF16>())) * kCtrLines * kLine * 4);
+  L.consumed = take(static_cast<size_t>(Hv) * ncg_of<D, BF16>() * kLine * 4);
+  L.ctr = take(static_cast<size_t>(launches(Hk, Hv, ncg_of<D, BF16>())) * kCtrLines * kLine * 4);
   L.total = off;
   return L;
 }
@@ -796,7 +795,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     dkf[hi * kC + lane] = __expf(glast - g);
     egt[hi * kC + lane] = __expf(g);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- L2 norm factors of q and k per token: 8 lanes per token, fixed order ----
   {
@@ -821,7 +820,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       inv[kC + r] = norm ? 1.0f / sqrtf(sk + A.l2_eps) : 1.0f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   auto qn = [&](int r, int d) { return qk[r * QK_LD + d] * inv[r]; };
   auto kn = [&](int r, int d) { return qk[r * QK_LD + D + d] * inv[kC + r]; };
   auto pack = [&](const float (&v)[EPL]) { return pack_lane<BF16>([&](int e) { return v[e]; }); };
@@ -868,7 +867,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     gt[Gm::G_G + ln] = gcum[hi * kC + ln];
     gt[Gm::G_EGL + ln] = __expf(gcum[hi * kC + kC - 1]);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- K K^T (lower 16x16 tiles) into L (one inverse group) or LDS; K Q^T
   // read as packed P tiles of every v-head (ring).  With a single inverse
@@ -881,27 +880,39 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     TriTiles<BF16>::at(pt, ti, ks);
     // (K Q^T)[j][r] with j = 16 tj + 4g + i, r = 16 ti + (lane & 15): the
     // accumulator of tile (tj, ti) is packed P tile (ti, ks) element (tj%TPS)*4 + i
+    // Every operand is read before the products and every LDS value before
+    // its use, with the masks applied last as selects: a lane never waits on
+    // one read at a time.
     f32x4_t acc[TPS];
+    Bop qb[KSD];
+#pragma unroll
+    for (int kd = 0; kd < KSD; ++kd) qb[kd] = __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]);
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
       const int tj = TPS * ks + u;
       acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
+        uint4 ka[KSD];
 #pragma unroll
-        for (int kd = 0; kd < KSD; ++kd)
-          acc[u] = Ch::step(kh_t[(tj * KSD + kd) * 64 + lane],
-                            __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]), acc[u]);
+        for (int kd = 0; kd < KSD; ++kd) ka[kd] = kh_t[(tj * KSD + kd) * 64 + lane];
+#pragma unroll
+        for (int kd = 0; kd < KSD; ++kd) acc[u] = Ch::step(ka[kd], qb[kd], acc[u]);
       }
     }
     const int r = 16 * ti + (lane & 15), g = lane >> 4;
     for (int hi = 0; hi < G; ++hi) {
       const float* gc = gcum + hi * kC;
       const float gr = gc[r];
-      float pv[EPL];
+      float gj[EPL], pv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) gj[e] = gc[ks * SK + (e >> 2) * 16 + 4 * g + (e & 3)];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) settle(gj[e]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
-        pv[e] = j <= r ? __expf(gr - gc[j]) * acc[e >> 2][e & 3] : 0.f;
+        const float v = __expf(j <= r ? gr - gj[e] : 0.f) * acc[e >> 2][e & 3];
+        pv[e] = j <= r ? v : 0.f;
       }
       *reinterpret_cast<uint4*>(htile(hi, Gm::HP + pt)) = pack(pv);
     }
@@ -917,14 +928,22 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
         // K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about fp32
         // accuracy, in three independent accumulators
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
+        uint4 ah[KSD], bh[KSD], al[KSD], bl[KSD];
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-          const uint4 ah = kh_t[(ti * KSD + ks) * 64 + lane];
-          const Bop bh = __builtin_bit_cast(Bop, kh_t[(tj * KSD + ks) * 64 + lane]);
-          acc = Ch::step(ah, bh, acc);
+          ah[ks] = kh_t[(ti * KSD + ks) * 64 + lane];
+          bh[ks] = kh_t[(tj * KSD + ks) * 64 + lane];
           if constexpr (BF16) {
-            acc1 = Ch::step(ah, __builtin_bit_cast(Bop, kl_t[(tj * KSD + ks) * 64 + lane]), acc1);
-            acc2 = Ch::step(kl_t[(ti * KSD + ks) * 64 + lane], bh, acc2);
+            al[ks] = kl_t[(ti * KSD + ks) * 64 + lane];
+            bl[ks] = kl_t[(tj * KSD + ks) * 64 + lane];
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          acc = Ch::step(ah[ks], __builtin_bit_cast(Bop, bh[ks]), acc);
+          if constexpr (BF16) {
+            acc1 = Ch::step(ah[ks], __builtin_bit_cast(Bop, bl[ks]), acc1);
+            acc2 = Ch::step(al[ks], __builtin_bit_cast(Bop, bh[ks]), acc2);
           }
         }
         if constexpr (BF16) acc = acc + (acc1 + acc2);
@@ -936,11 +955,23 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
           for (int hi = 0; hi < G; ++hi) {
             const float* gc = gcum + hi * kC;
             const float gj = gc[j];
+            float gr[4], br[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              gr[i] = gc[16 * ti + 4 * g + i];
+              br[i] = bet[hi * kC + 16 * ti + 4 * g + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              settle(gr[i]);
+              settle(br[i]);
+            }
             float* Lh = Lt + hi * kC * kLd;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 16 * ti + 4 * g + i;
-              Lh[r * kLd + j] = j < r ? bet[hi * kC + r] * __expf(gc[r] - gj) * acc[i] : 0.f;
+              const float v = br[i] * __expf(j < r ? gr[i] - gj : 0.f) * acc[i];
+              Lh[r * kLd + j] = j < r ? v : 0.f;
               if (ti != tj) Lh[(16 * tj + 4 * g + i) * kLd + 16 * ti + (lane & 15)] = 0.f;
             }
           }
@@ -953,7 +984,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- per group of NH v-heads: L, T = (I + L)^{-1}, then T diag(beta) ----
   for (int hg0 = 0; hg0 < G; hg0 += NH) {
@@ -962,16 +993,22 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       for (int e = tid; e < nh * kC * kC; e += kThreads) {
         const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
         const float* gc = gcum + (hg0 + i) * kC;
-        Lt[i * kC * kLd + r * kLd + j] = j < r ? bet[(hg0 + i) * kC + r] * __expf(gc[r] - gc[j]) * Am[r * kLd + j] : 0.f;
+        float br = bet[(hg0 + i) * kC + r], grv = gc[r], gjv = gc[j], kk = Am[r * kLd + j];
+        settle(br);
+        settle(grv);
+        settle(gjv);
+        settle(kk);
+        const float v = br * __expf(j < r ? grv - gjv : 0.f) * kk;
+        Lt[i * kC * kLd + r * kLd + j] = j < r ? v : 0.f;
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (wave < nh) {
       invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
     } else if (p_later) {
       for (int pt = wave - nh; pt < NTRI; pt += kWaves - nh) p_task(pt);
     }
-    __syncthreads();
+    lds_barrier();
     // T diag(beta) as A tiles (rows r, k = j); only the tiles of the lower triangle
     for (int u = tid; u < nh * NTRI * 64; u += kThreads) {
       const int i = (u >> 6) / NTRI, t = (u >> 6) % NTRI, ln = u & 63;
@@ -980,16 +1017,28 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       const int r = 16 * mt + (ln & 15), g = ln >> 4;
       const float* Ti = Lt + i * kC * kLd + r * kLd;
       const float* sc = bet + (hg0 + i) * kC;
-      float tv[EPL];
+      float tv[EPL], tl[EPL], bj[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
-        tv[e] = j <= r ? Ti[j] * sc[j] : 0.f;
+        tl[e] = Ti[j];  // any value above the diagonal; masked below
+        bj[e] = sc[j];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        settle(tl[e]);
+        settle(bj[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        const float v = tl[e] * bj[e];
+        tv[e] = j <= r ? v : 0.f;
       }
       *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::HEAD0 + (hg0 + i) * Gm::HEAD_TILES + Gm::HT + t) *
                                          kTileBytes + 16 * ln) = pack(tv);
     }
-    __syncthreads();  // Lt is reused by the next group
+    lds_barrier();  // Lt is reused by the next group
   }
 
   // ---- publish (chunk, k-head): every wave's stores have reached the L2
@@ -1479,7 +1528,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 // values live; the plain prefill does not carry them).
 template <int D, bool BF16, int KW, bool CKPT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, PrefillLayout L) {
-  constexpr int NCG = CKPT ? ncg_ckpt<D, BF16>() : 1;
+  constexpr int NCG = ncg_of<D, BF16>();
   __shared__ __attribute__((aligned(1024))) char smem[SmemBytes<D, BF16, NCG>::value];
   __shared__ int s_tk[2];
   const int tid = threadIdx.x;
@@ -1538,7 +1587,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
 template <int D, bool BF16>
 static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st) {
   const PrefillLayout L = layout_t<D, BF16>(a0.Hk, a0.Hv, a0.n_tokens, a0.n_seqs);
-  const int ncg = a0.ckpt_every > 0 ? ncg_ckpt<D, BF16>() : 1;  // as the kernel variant chosen below
+  const int ncg = ncg_of<D, BF16>();
   const int n_launch = launches(a0.Hk, a0.Hv, ncg);
   const int per = heads_per_launch(a0.Hk, a0.Hv, ncg);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L, n_launch);
