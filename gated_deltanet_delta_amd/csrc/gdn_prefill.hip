@@ -394,14 +394,35 @@ struct Chain<false> {
   }
 };
 
-// acc += A (16x16, row-major at a, stride lda) * B (16x16, row-major at b, stride ldb); fp32.
-__device__ __forceinline__ f32x4_t prod16(const float* a, int lda, const float* b, int ldb,
-                                          f32x4_t acc, int lane) {
+// 16x16 fp32 tiles as MFMA operands (v_mfma_f32_16x16x4_f32, four steps):
+// A row-major at a (stride lda), lane = row (lane & 15); step s contracts
+// index 4 s + (lane >> 4).  An accumulator tile (lane: rows 4 (lane >> 4) + i
+// of column lane & 15) can be the B operand as it is when its A partner is
+// read with step s contracting index 4 (lane >> 4) + s instead ("acc order").
+__device__ __forceinline__ f32x4_t tile_a(const float* a, int lda, int lane) {
+  f32x4_t v;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = mfma4(a[(lane & 15) * lda + 4 * s + (lane >> 4)], b[(4 * s + (lane >> 4)) * ldb + (lane & 15)], acc);
+  for (int s = 0; s < 4; ++s) v[s] = a[(lane & 15) * lda + 4 * s + (lane >> 4)];
+  return v;
+}
+__device__ __forceinline__ f32x4_t tile_a_acc(const float* a, int lda, int lane) {
+  f32x4_t v;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v[s] = a[(lane & 15) * lda + 4 * (lane >> 4) + s];
+  return v;
+}
+__device__ __forceinline__ f32x4_t tile_b(const float* b, int ldb, int lane) {
+  f32x4_t v;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v[s] = b[(4 * s + (lane >> 4)) * ldb + (lane & 15)];
+  return v;
+}
+__device__ __forceinline__ f32x4_t mm16(const f32x4_t& a, const f32x4_t& b, f32x4_t acc) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma4(a[s], b[s], acc);
   return acc;
 }
+__device__ __forceinline__ void settle4(f32x4_t& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ void store16(float* d, int ld, f32x4_t v, float sign, int lane) {
 #pragma unroll
@@ -411,61 +432,97 @@ __device__ __forceinline__ void store16(float* d, int ld, f32x4_t v, float sign,
 // In-place inverse of the unit lower-triangular I + L (64x64, L strictly lower,
 // row stride kLd) by one wave: 16x16 diagonal blocks by forward substitution
 // (lane = block x column), then the off-diagonal blocks level by level with
-// fp32 MFMA:  [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1].
-// tmp: 32 x 33 floats of scratch.
-__device__ __forceinline__ void invert_unit_lower64(float* Lt, float* tmp, int lane) {
+// fp32 MFMA:  [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1].  Every stage reads
+// all its LDS operands before its arithmetic, and each level's inner product
+// C A^-1 feeds the outer one from registers.
+__device__ __forceinline__ void invert_unit_lower64(float* Lt, int lane) {
   {
+    // column by column: once t_j is final, every later row takes its term;
+    // the strictly lower triangle of the block is read first
     const int bi = lane >> 4, c = lane & 15;
     float* Lb = Lt + 16 * bi * kLd + 16 * bi;
+    float l[16][16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int j = 0; j < r; ++j) l[r][j] = Lb[r * kLd + j];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int j = 0; j < r; ++j) settle(l[r][j]);
     float t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == c) ? 1.0f : 0.0f;
+    for (int r = 0; r < 16; ++r) t[r] = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int j = 0; j < r; ++j) acc = fmaf(-Lb[r * kLd + j], t[j], acc);
-      t[r] = acc;
-    }
+    for (int j = 0; j < 15; ++j)
+#pragma unroll
+      for (int r = j + 1; r < 16; ++r) t[r] = fmaf(-l[r][j], t[j], t[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) Lb[r * kLd + c] = t[r];
   }
-  // 32x32 level: T10 = -T11 (L10 T00) in both diagonal 32-blocks
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  // 32x32 level, diagonal 32-blocks b = 0, 1: T10 = -T11 (L10 T00)
+  {
+    f32x4_t a[2], bt[2], m[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float* o = Lt + 32 * b * kLd + 32 * b;
-    f32x4_t m = prod16(o + 16 * kLd, kLd, o, kLd, f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
-    store16(tmp, 17, m, 1.0f, lane);
-    f32x4_t r = prod16(o + 16 * kLd + 16, kLd, tmp, 17, f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
-    store16(o + 16 * kLd, kLd, r, -1.0f, lane);
+    for (int b = 0; b < 2; ++b) {
+      const float* o = Lt + 32 * b * kLd + 32 * b;
+      a[b] = tile_a(o + 16 * kLd, kLd, lane);
+      bt[b] = tile_b(o, kLd, lane);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      settle4(a[b]);
+      settle4(bt[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) m[b] = mm16(a[b], bt[b], zero);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) a[b] = tile_a_acc(Lt + (32 * b + 16) * kLd + 32 * b + 16, kLd, lane);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) settle4(a[b]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) store16(Lt + (32 * b + 16) * kLd + 32 * b, kLd, mm16(a[b], m[b], zero), -1.0f, lane);
   }
-  // 64x64 level: T_BA = -T_B (C T_A), 32x32 blocks; C is the lower-left block of L
+  // 64x64 level: T_BA = -T_B (C T_A), 32x32 blocks of 16x16 tiles; C is the
+  // lower-left block of L; T_A[0][1] = 0 and T_B[0][1] = 0
   const float* C = Lt + 32 * kLd;
-  const float* TA = Lt;
   const float* TB = Lt + 32 * kLd + 32;
   f32x4_t m2[2][2];
+  {
+    f32x4_t ca[2][2], ta[3];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) ca[rt][kt] = tile_a(C + 16 * rt * kLd + 16 * kt, kLd, lane);
+    ta[0] = tile_b(Lt, kLd, lane);                  // T_A[0][0]
+    ta[1] = tile_b(Lt + 16 * kLd, kLd, lane);       // T_A[1][0]
+    ta[2] = tile_b(Lt + 16 * kLd + 16, kLd, lane);  // T_A[1][1]
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) settle4(ca[rt][kt]);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) settle4(ta[i]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      m2[rt][0] = mm16(ca[rt][1], ta[1], mm16(ca[rt][0], ta[0], zero));
+      m2[rt][1] = mm16(ca[rt][1], ta[2], zero);
+    }
+  }
+  {
+    f32x4_t tb[3];
+    tb[0] = tile_a_acc(TB, kLd, lane);                  // T_B[0][0]
+    tb[1] = tile_a_acc(TB + 16 * kLd, kLd, lane);       // T_B[1][0]
+    tb[2] = tile_a_acc(TB + 16 * kLd + 16, kLd, lane);  // T_B[1][1]
+#pragma unroll
+    for (int i = 0; i < 3; ++i) settle4(tb[i]);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = ct; kt < 2; ++kt)  // T_A[kt][ct] = 0 for kt < ct
-        acc = prod16(C + 16 * rt * kLd + 16 * kt, kLd, TA + 16 * kt * kLd + 16 * ct, kLd, acc, lane);
-      m2[rt][ct] = acc;
+      store16(Lt + 32 * kLd + 16 * ct, kLd, mm16(tb[0], m2[0][ct], zero), -1.0f, lane);
+      store16(Lt + 48 * kLd + 16 * ct, kLd, mm16(tb[2], m2[1][ct], mm16(tb[1], m2[0][ct], zero)), -1.0f, lane);
     }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) store16(tmp + 16 * rt * 33 + 16 * ct, 33, m2[rt][ct], 1.0f, lane);
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt <= rt; ++kt)  // T_B[rt][kt] = 0 for kt > rt
-        acc = prod16(TB + 16 * rt * kLd + 16 * kt, kLd, tmp + 16 * kt * 33 + 16 * ct, 33, acc, lane);
-      store16(Lt + (32 + 16 * rt) * kLd + 16 * ct, kLd, acc, -1.0f, lane);
-    }
+  }
 }
 
 template <bool BF16>
@@ -609,7 +666,7 @@ __device__ __forceinline__ ChunkPos chunk_pos(const int32_t* se, int ci) {
 // producer: one (chunk, k-head) item
 // ---------------------------------------------------------------------------
 // LDS of the producer, by lifetime:
-//   R0: conv outputs of q | k (fp32), then L -> T and inverse scratch of NH heads
+//   R0: conv outputs of q | k (fp32), then L -> T of NH heads
 //   R1: k (hi, lo for bf16) and q as A tiles
 //   AM: K K^T (several inverse groups only);  MISC: per-token gate tables and norm factors
 template <int D, bool BF16>
@@ -619,9 +676,8 @@ struct ProdSmem {
   static constexpr int QK_LD = 2 * D + 4;            // rows 16-byte aligned
   static constexpr int PK_Q = BF16 ? 2 : 1;          // index of the q tiles in R1
   static constexpr size_t LT1 = static_cast<size_t>(kC) * kLd * 4;
-  static constexpr size_t SCR1 = 32 * 33 * 4;
   static constexpr size_t R0A = static_cast<size_t>(kC) * QK_LD * 4;
-  static constexpr size_t R0B = NH * (LT1 + SCR1);
+  static constexpr size_t R0B = NH * LT1;
   static constexpr size_t R0 = R0A > R0B ? R0A : R0B;
   static constexpr size_t R1 = (PK_Q + 1) * 4 * Gm::KSD * kTileBytes;
   static constexpr size_t AM = LT1;
@@ -650,7 +706,6 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   float* smem = reinterpret_cast<float*>(sb);
   float* qk = smem;                                        // [64][QK_LD] conv outputs of q | k
   float* Lt = smem;                                        // NH x [64][65]: L -> T
-  float* tmpw = smem + NH * kC * kLd;                      // NH x [32][33] inverse scratch
   uint4* pk = reinterpret_cast<uint4*>(sb + Sm::R0);       // k (hi, lo) and q as A tiles
   float* Am = reinterpret_cast<float*>(sb + Sm::R0 + Sm::R1);  // [64][65] K K^T
   float* gcum = Am + kC * kLd;                             // [8][64] G
@@ -869,9 +924,9 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   }
   lds_barrier();
 
-  // ---- K K^T (lower 16x16 tiles) into L (one inverse group) or LDS; K Q^T
-  // read as packed P tiles of every v-head (ring).  With a single inverse
-  // group the P tasks run on the waves the inverse leaves idle. ----
+  // ---- K K^T (lower 16x16 tiles) into L (one inverse group) or LDS, and K Q^T
+  // read as packed P tiles of every v-head (ring): 10 + NTRI tasks over the
+  // waves, so the inverses that follow have the CU to themselves. ----
   const uint4* kh_t = pk;
   const uint4* kl_t = pk + 4 * KSD * 64;
   const uint4* q_t = pk + Sm::PK_Q * 4 * KSD * 64;
@@ -917,9 +972,8 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       *reinterpret_cast<uint4*>(htile(hi, Gm::HP + pt)) = pack(pv);
     }
   };
-  const bool p_later = G <= NH;
   {
-    const int ntask = p_later ? 10 : 10 + NTRI;
+    const int ntask = 10 + NTRI;
     for (int task = wave; task < ntask; task += kWaves) {
       if (task < 10) {
         int t = task, ti = 0;
@@ -1004,9 +1058,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       lds_barrier();
     }
     if (wave < nh) {
-      invert_unit_lower64(Lt + wave * kC * kLd, tmpw + wave * 32 * 33, lane);
-    } else if (p_later) {
-      for (int pt = wave - nh; pt < NTRI; pt += kWaves - nh) p_task(pt);
+      invert_unit_lower64(Lt + wave * kC * kLd, lane);
     }
     lds_barrier();
     // T diag(beta) as A tiles (rows r, k = j); only the tiles of the lower triangle
