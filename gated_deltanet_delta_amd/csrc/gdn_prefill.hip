@@ -735,21 +735,27 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
 
   // The ring slot is free once every chain workgroup of this k-head has staged
   // the chunk it held (RS chunks earlier).  One thread waits; the barrier
-  // keeps every wave's stores to the slot behind that wait.
-  if (chunk >= RS) {
-    if (tid == 0) {
-      const int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
-      for (int hh = 0; hh < G * NCG; ++hh)
-        if (!wait_at_least(consumed + (kh * G * NCG + hh) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err))
-          break;
+  // keeps every wave's stores to the slot behind that wait.  It comes after
+  // the conv's first input rows are requested, so they arrive during it.
+  // Lane i of wave 0 polls chain i's counter, so all of them are read in one
+  // round trip.
+  static_assert(kMaxGroup * NCG <= 64, "one lane per chain of the k-head");
+  auto wait_slot = [&]() {
+    if (chunk >= RS) {
+      if (wave == 0 && lane < G * NCG) {
+        const int32_t* consumed = ws_ptr<int32_t>(A.workspace, Lay.consumed);
+        wait_at_least(consumed + (kh * G * NCG + lane) * kLine, chunk - RS + 1, hdr + HDR_ABORT, A.dev_err);
+      }
+      lds_barrier();
     }
-    lds_barrier();
-  }
+  };
 
-  // gate inputs of the v-head whose gates this wave computes (the first G
-  // waves, one head each), loaded before the conv so they arrive under it
+  // gate inputs of the v-head whose gates this wave computes (the last G
+  // waves, one head each: they have the fewest conv items, so the gates run
+  // while the first waves finish theirs), loaded before the conv so they
+  // arrive under it
   static_assert(kMaxGroup <= kWaves, "one gate head per wave");
-  const int ghi = wave;
+  const int ghi = kWaves - 1 - wave;
   E a_raw{}, b_raw{};
   if (ghi < G && lane < len) {
     const size_t i = static_cast<size_t>(t0 + lane) * Hv + kh * G + ghi;
@@ -788,6 +794,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
           load_rows<BF16, KW>(A, c0, tq, cp, raw[k]);
         }
       }
+      if (base == 0) wait_slot();  // before the first ring store
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         const int item = base + k * kThreads + tid;
