@@ -693,8 +693,12 @@ struct SmemBytes {
   static_assert(value <= 158 * 1024, "LDS plan exceeds the CU's LDS");
 };
 
+// The workgroup's next ticket is taken from tctr at the start and left in
+// *next_ticket (LDS) before the final barrier, so no round trip separates
+// one item from the next.
 template <int D, bool BF16, int KW, int NCG>
-__device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int chunk, int kh) {
+__device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int chunk, int kh,
+                        int32_t* tctr, int* next_ticket) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ProdSmem<D, BF16>;
@@ -718,6 +722,8 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk;
   const int RS = Lay.ring_slots;
   int32_t* hdr = ws_ptr<int32_t>(A.workspace, Lay.hdr);
+  int32_t nxt = 0;
+  if (tid == 0) nxt = atomicAdd(tctr, 1);
   // the chunk's sequence: the last s whose first chunk is <= chunk
   const int32_t* stab = ws_ptr<int32_t>(A.workspace, Lay.seq_tab);
   int lo = 0, hi_s = A.n_seqs - 1;
@@ -1104,6 +1110,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   // (stores are acknowledged by the L2), then one flag store.  The readers are
   // on this XCD and read through the same L2. ----
   wait_stores();
+  if (tid == 0) *next_ticket = nxt;
   __syncthreads();
   if (tid == 0) {
     int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
@@ -1612,14 +1619,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
     chain_role<D, BF16, KW, CKPT, NCG>(A, L, smem, kh, kh * G + r / NCG, r % NCG);
     chain_done = 1;
   } else if (nk > 0) {
+    // Items of this XCD in chunk order; each item takes the next ticket.
     const int n_items = total * nk;
-    for (;;) {
-      __syncthreads();  // s_tk is free
-      if (tid == 0) s_tk[1] = atomicAdd(ctr + (kXcd + xcc) * kLine, 1);
-      __syncthreads();
-      const int it = s_tk[1];
-      if (it >= n_items) break;
-      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk));
+    int32_t* tctr = ctr + (kXcd + xcc) * kLine;
+    __syncthreads();  // s_tk is free
+    if (tid == 0) s_tk[1] = atomicAdd(tctr, 1);
+    __syncthreads();
+    for (int it = s_tk[1]; it < n_items; it = s_tk[1]) {
+      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk), tctr, &s_tk[1]);
       ++items_done;
     }
   }
