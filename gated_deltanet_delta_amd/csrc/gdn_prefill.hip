@@ -666,9 +666,9 @@ __device__ __forceinline__ ChunkPos chunk_pos(const int32_t* se, int ci) {
 // producer: one (chunk, k-head) item
 // ---------------------------------------------------------------------------
 // LDS of the producer, by lifetime:
-//   R0: conv outputs of q | k (fp32), then L -> T of NH heads
+//   R0: conv outputs of q | k (fp32), then L -> T of NH heads and Q K^T
 //   R1: k (hi, lo for bf16) and q as A tiles
-//   AM: K K^T (several inverse groups only);  MISC: per-token gate tables and norm factors
+//   AM: K K^T;  MISC: per-token gate tables and norm factors
 template <int D, bool BF16>
 struct ProdSmem {
   using Gm = Geo<D, BF16>;
@@ -677,7 +677,7 @@ struct ProdSmem {
   static constexpr int PK_Q = BF16 ? 2 : 1;          // index of the q tiles in R1
   static constexpr size_t LT1 = static_cast<size_t>(kC) * kLd * 4;
   static constexpr size_t R0A = static_cast<size_t>(kC) * QK_LD * 4;
-  static constexpr size_t R0B = NH * LT1;
+  static constexpr size_t R0B = (NH + 1) * LT1;
   static constexpr size_t R0 = R0A > R0B ? R0A : R0B;
   static constexpr size_t R1 = (PK_Q + 1) * 4 * Gm::KSD * kTileBytes;
   static constexpr size_t AM = LT1;
@@ -710,6 +710,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   float* smem = reinterpret_cast<float*>(sb);
   float* qk = smem;                                        // [64][QK_LD] conv outputs of q | k
   float* Lt = smem;                                        // NH x [64][65]: L -> T
+  float* QKm = smem + NH * kC * kLd;                       // [64][65] Q K^T
   uint4* pk = reinterpret_cast<uint4*>(sb + Sm::R0);       // k (hi, lo) and q as A tiles
   float* Am = reinterpret_cast<float*>(sb + Sm::R0 + Sm::R1);  // [64][65] K K^T
   float* gcum = Am + kC * kLd;                             // [8][64] G
@@ -937,118 +938,92 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   }
   lds_barrier();
 
-  // ---- K K^T (lower 16x16 tiles) into L (one inverse group) or LDS, and K Q^T
-  // read as packed P tiles of every v-head (ring): 10 + NTRI tasks over the
-  // waves, so the inverses that follow have the CU to themselves. ----
+  // ---- K K^T and Q K^T, lower 16x16 tiles (ti >= tj), into LDS (fp32): one
+  // task per tile.  K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about
+  // fp32 accuracy, in three independent accumulators. ----
   const uint4* kh_t = pk;
   const uint4* kl_t = pk + 4 * KSD * 64;
   const uint4* q_t = pk + Sm::PK_Q * 4 * KSD * 64;
-  auto p_task = [&](int pt) {
-    int ti, ks;
-    TriTiles<BF16>::at(pt, ti, ks);
-    // (K Q^T)[j][r] with j = 16 tj + 4g + i, r = 16 ti + (lane & 15): the
-    // accumulator of tile (tj, ti) is packed P tile (ti, ks) element (tj%TPS)*4 + i
-    // Every operand is read before the products and every LDS value before
-    // its use, with the masks applied last as selects: a lane never waits on
-    // one read at a time.
-    f32x4_t acc[TPS];
-    Bop qb[KSD];
+  for (int task = wave; task < 10; task += kWaves) {
+    int t = task, ti = 0;
+    while (t > ti) { t -= ti + 1; ++ti; }
+    const int tj = t;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc, accq = acc;
+    uint4 ah[KSD], bh[KSD], al[KSD], bl[KSD], qa[KSD];
 #pragma unroll
-    for (int kd = 0; kd < KSD; ++kd) qb[kd] = __builtin_bit_cast(Bop, q_t[(ti * KSD + kd) * 64 + lane]);
-#pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-      const int tj = TPS * ks + u;
-      acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (tj <= ti) {
-        uint4 ka[KSD];
-#pragma unroll
-        for (int kd = 0; kd < KSD; ++kd) ka[kd] = kh_t[(tj * KSD + kd) * 64 + lane];
-#pragma unroll
-        for (int kd = 0; kd < KSD; ++kd) acc[u] = Ch::step(ka[kd], qb[kd], acc[u]);
+    for (int ks = 0; ks < KSD; ++ks) {
+      ah[ks] = kh_t[(ti * KSD + ks) * 64 + lane];
+      bh[ks] = kh_t[(tj * KSD + ks) * 64 + lane];
+      qa[ks] = q_t[(ti * KSD + ks) * 64 + lane];
+      if constexpr (BF16) {
+        al[ks] = kl_t[(ti * KSD + ks) * 64 + lane];
+        bl[ks] = kl_t[(tj * KSD + ks) * 64 + lane];
       }
     }
-    const int r = 16 * ti + (lane & 15), g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      acc = Ch::step(ah[ks], __builtin_bit_cast(Bop, bh[ks]), acc);
+      accq = Ch::step(qa[ks], __builtin_bit_cast(Bop, bh[ks]), accq);
+      if constexpr (BF16) {
+        acc1 = Ch::step(ah[ks], __builtin_bit_cast(Bop, bl[ks]), acc1);
+        acc2 = Ch::step(al[ks], __builtin_bit_cast(Bop, bh[ks]), acc2);
+      }
+    }
+    if constexpr (BF16) acc = acc + (acc1 + acc2);
+    const int g = lane >> 4, j = 16 * tj + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Am[(16 * ti + 4 * g + i) * kLd + j] = acc[i];
+      QKm[(16 * ti + 4 * g + i) * kLd + j] = accq[i];
+    }
+  }
+  lds_barrier();
+
+  // ---- per (packed P tile, lane): row r, EPL columns j; the decay
+  // e^{G_r - G_j} of each v-head serves both P_rj = e^{G_r - G_j} (q_r . k_j),
+  // j <= r (ring, every v-head) and L_rj = beta_r e^{G_r - G_j} (k_r . k_j),
+  // j < r (LDS, the first inverse group).  The tiles cover every j < r. ----
+  for (int u = tid; u < NTRI * 64; u += kThreads) {
+    const int pt = u >> 6, ln = u & 63;
+    int mt, ks;
+    TriTiles<BF16>::at(pt, mt, ks);
+    const int r = 16 * mt + (ln & 15), g = ln >> 4;
+    float kk[EPL], qq[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+      kk[e] = Am[r * kLd + j];  // any value at j >= r; masked below
+      qq[e] = QKm[r * kLd + j];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      settle(kk[e]);
+      settle(qq[e]);
+    }
     for (int hi = 0; hi < G; ++hi) {
       const float* gc = gcum + hi * kC;
-      const float gr = gc[r];
-      float gj[EPL], pv[EPL];
+      float gr = gc[r], br = bet[hi * kC + r], gj[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) gj[e] = gc[ks * SK + (e >> 2) * 16 + 4 * g + (e & 3)];
+      settle(gr);
+      settle(br);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) settle(gj[e]);
+      float pv[EPL];
+      float* Lr = Lt + hi * kC * kLd + r * kLd;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int j = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
-        const float v = __expf(j <= r ? gr - gj[e] : 0.f) * acc[e >> 2][e & 3];
-        pv[e] = j <= r ? v : 0.f;
+        const float d = __expf(j <= r ? gr - gj[e] : 0.f);
+        const float pvv = d * qq[e];
+        pv[e] = j <= r ? pvv : 0.f;
+        if (hi < NH) {
+          const float lv = br * d * kk[e];
+          Lr[j] = j < r ? lv : 0.f;
+        }
       }
-      *reinterpret_cast<uint4*>(htile(hi, Gm::HP + pt)) = pack(pv);
-    }
-  };
-  {
-    const int ntask = 10 + NTRI;
-    for (int task = wave; task < ntask; task += kWaves) {
-      if (task < 10) {
-        int t = task, ti = 0;
-        while (t > ti) { t -= ti + 1; ++ti; }
-        const int tj = t;
-        // K K^T feeds the inverse: hi*hi + hi*lo + lo*hi for about fp32
-        // accuracy, in three independent accumulators
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
-        uint4 ah[KSD], bh[KSD], al[KSD], bl[KSD];
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          ah[ks] = kh_t[(ti * KSD + ks) * 64 + lane];
-          bh[ks] = kh_t[(tj * KSD + ks) * 64 + lane];
-          if constexpr (BF16) {
-            al[ks] = kl_t[(ti * KSD + ks) * 64 + lane];
-            bl[ks] = kl_t[(tj * KSD + ks) * 64 + lane];
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          acc = Ch::step(ah[ks], __builtin_bit_cast(Bop, bh[ks]), acc);
-          if constexpr (BF16) {
-            acc1 = Ch::step(ah[ks], __builtin_bit_cast(Bop, bl[ks]), acc1);
-            acc2 = Ch::step(al[ks], __builtin_bit_cast(Bop, bh[ks]), acc2);
-          }
-        }
-        if constexpr (BF16) acc = acc + (acc1 + acc2);
-        const int g = lane >> 4, j = 16 * tj + (lane & 15);
-        if (G <= NH) {
-          // one inverse group: L_rj = beta_r e^{G_r - G_j} (k_r . k_j), r > j, of every
-          // v-head straight from the accumulator; the mirrored block above the
-          // diagonal is zero
-          for (int hi = 0; hi < G; ++hi) {
-            const float* gc = gcum + hi * kC;
-            const float gj = gc[j];
-            float gr[4], br[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              gr[i] = gc[16 * ti + 4 * g + i];
-              br[i] = bet[hi * kC + 16 * ti + 4 * g + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              settle(gr[i]);
-              settle(br[i]);
-            }
-            float* Lh = Lt + hi * kC * kLd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * ti + 4 * g + i;
-              const float v = br[i] * __expf(j < r ? gr[i] - gj : 0.f) * acc[i];
-              Lh[r * kLd + j] = j < r ? v : 0.f;
-              if (ti != tj) Lh[(16 * tj + 4 * g + i) * kLd + 16 * ti + (lane & 15)] = 0.f;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Am[(ti * 16 + g * 4 + i) * kLd + j] = acc[i];
-        }
-      } else {
-        p_task(task - 10);
-      }
+      *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::HEAD0 + hi * Gm::HEAD_TILES + Gm::HP + pt) * kTileBytes +
+                                16 * ln) = pack(pv);
     }
   }
   lds_barrier();
@@ -1056,7 +1031,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   // ---- per group of NH v-heads: L, T = (I + L)^{-1}, then T diag(beta) ----
   for (int hg0 = 0; hg0 < G; hg0 += NH) {
     const int nh = min(NH, G - hg0);
-    if (G > NH) {  // several groups: L of this group from K K^T in LDS
+    if (hg0 > 0) {  // later groups: L of this group from K K^T in LDS
       for (int e = tid; e < nh * kC * kC; e += kThreads) {
         const int i = e / (kC * kC), r = (e / kC) % kC, j = e % kC;
         const float* gc = gcum + (hg0 + i) * kC;
