@@ -662,6 +662,60 @@ __device__ __forceinline__ ChunkPos chunk_pos(const int32_t* se, int ci) {
   return p;
 }
 
+// Where chunk `chunk` of the call lies: its sequence is the last s whose
+// first chunk is <= chunk.
+__device__ __forceinline__ ChunkPos item_pos(const PrefillArgs& A, const PrefillLayout& Lay, int chunk) {
+  const int32_t* stab = ws_ptr<int32_t>(A.workspace, Lay.seq_tab);
+  int lo = 0, hi_s = A.n_seqs - 1;
+  while (lo < hi_s) {
+    const int mid = (lo + hi_s + 1) >> 1;
+    if (stab[8 * mid + SQ_FIRST] <= chunk) lo = mid; else hi_s = mid - 1;
+  }
+  const int32_t* se = stab + 8 * lo;
+  return chunk_pos(se, chunk - se[SQ_FIRST]);
+}
+
+// Conv item `item` of k-head kh: item = (2 channels, 16 tokens), the q | k
+// items (4 D of them) first, then the v items of the k-head's G v-heads.
+// Returns the first channel; tq = the item's first token within the chunk.
+template <int D>
+__device__ __forceinline__ int conv_item_c0(int item, int kh, int Hk, int G, int& tq) {
+  constexpr int NQK = 4 * D;
+  if (item < NQK) {
+    const int q = item / D, cc0 = 2 * (item % D);
+    tq = 16 * q;
+    return cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
+  }
+  const int i2 = item - NQK;
+  tq = 16 * (i2 / (G * D / 2));
+  return 2 * Hk * D + kh * G * D + 2 * (i2 % (G * D / 2));
+}
+
+// The conv inputs of a later item (chunk, kh) requested into the L2, so that
+// its conv finds them there: one 4-byte load per 64-byte line of the rows it
+// reads (its q, k and v channels, tokens t0 - 3 .. t0 + len - 1 within the
+// sequence), straight into a scratch LDS slot of the wave (no registers
+// held), by threads t, t + nthr, ...
+template <int D, bool BF16>
+__device__ void prefetch_item_rows(const PrefillArgs& A, const PrefillLayout& Lay, int chunk, int kh, int t,
+                                   int nthr, void* lds_slot) {
+  using E = typename Pk<BF16>::E;
+  constexpr int EPL64 = 64 / static_cast<int>(sizeof(E));  // channels per 64-byte line
+  const ChunkPos cp = item_pos(A, Lay, chunk);
+  const int G = A.Hv / A.Hk;
+  const int lq = (D + EPL64 - 1) / EPL64, lv = (G * D + EPL64 - 1) / EPL64, per_row = 2 * lq + lv;
+  const int r0 = max(cp.t0 - 3, cp.seq_start), nrow = cp.t0 + cp.len - r0;
+  const E* x = static_cast<const E*>(A.x);
+  for (int i = t; i < nrow * per_row; i += nthr) {
+    const int row = r0 + i / per_row, l = i % per_row;
+    const int ch = l < lq ? kh * D + l * EPL64
+                          : (l < 2 * lq ? A.Hk * D + kh * D + (l - lq) * EPL64
+                                        : 2 * A.Hk * D + kh * G * D + (l - 2 * lq) * EPL64);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(x + static_cast<size_t>(row) * A.C + ch),
+                                     (__attribute__((address_space(3))) void*)(lds_slot), 4, 0, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // producer: one (chunk, k-head) item
 // ---------------------------------------------------------------------------
@@ -694,11 +748,12 @@ struct SmemBytes {
 };
 
 // The workgroup's next ticket is taken from tctr at the start and left in
-// *next_ticket (LDS) before the final barrier, so no round trip separates
-// one item from the next.
+// *next_ticket (LDS) half-way, so no round trip separates one item from the
+// next, and the next item's conv inputs are requested while this one inverts.
+// A ticket t < n_tickets is item (t / nk, kh_base + 8 (t % nk)).
 template <int D, bool BF16, int KW, int NCG>
 __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int chunk, int kh,
-                        int32_t* tctr, int* next_ticket) {
+                        int32_t* tctr, int* next_ticket, int nk, int n_tickets, int kh_base) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ProdSmem<D, BF16>;
@@ -725,15 +780,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   int32_t* hdr = ws_ptr<int32_t>(A.workspace, Lay.hdr);
   int32_t nxt = 0;
   if (tid == 0) nxt = atomicAdd(tctr, 1);
-  // the chunk's sequence: the last s whose first chunk is <= chunk
-  const int32_t* stab = ws_ptr<int32_t>(A.workspace, Lay.seq_tab);
-  int lo = 0, hi_s = A.n_seqs - 1;
-  while (lo < hi_s) {
-    const int mid = (lo + hi_s + 1) >> 1;
-    if (stab[8 * mid + SQ_FIRST] <= chunk) lo = mid; else hi_s = mid - 1;
-  }
-  const int32_t* se = stab + 8 * lo;
-  const ChunkPos cp = chunk_pos(se, chunk - se[SQ_FIRST]);
+  const ChunkPos cp = item_pos(A, Lay, chunk);
   const int t0 = cp.t0, len = cp.len;
   char* rb = static_cast<char*>(A.workspace) + Lay.ring +
              (static_cast<size_t>(chunk % RS) * Hk + kh) * Lay.item_bytes;
@@ -780,16 +827,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     constexpr int NQK = 4 * D;             // 2 D channels / 2 per item x 4 quarters
     constexpr int NB = BF16 ? 3 : 2;       // rounds whose loads are in flight together
     const int n_items = NQK + 2 * G * D;   // + G D v channels / 2 x 4 quarters
-    auto item_c0 = [&](int item, int& tq) {
-      if (item < NQK) {
-        const int q = item / D, cc0 = 2 * (item % D);
-        tq = 16 * q;
-        return cc0 < D ? kh * D + cc0 : Hk * D + kh * D + (cc0 - D);
-      }
-      const int i2 = item - NQK;
-      tq = 16 * (i2 / (G * D / 2));
-      return 2 * Hk * D + kh * G * D + 2 * (i2 % (G * D / 2));
-    };
+    auto item_c0 = [&](int item, int& tq) { return conv_item_c0<D>(item, kh, Hk, G, tq); };
     for (int base = 0; base < n_items; base += NB * kThreads) {
       Rows<BF16> raw[NB];
 #pragma unroll
@@ -977,7 +1015,21 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       QKm[(16 * ti + 4 * g + i) * kLd + j] = accq[i];
     }
   }
+  if (tid == 0) *next_ticket = nxt;
   lds_barrier();
+
+  // The waves without work in the next phase (first_wave and up) request the
+  // next item's conv inputs into the L2; their LDS slots lie in the packed
+  // tiles, which are no longer read.
+  auto prefetch_next = [&](int first_wave) {
+    if (wave >= first_wave) {
+      const int t = *next_ticket;
+      if (t < n_tickets)
+        prefetch_item_rows<D, BF16>(A, Lay, t / nk, kh_base + kXcd * (t % nk), tid - first_wave * 64,
+                                    (kWaves - first_wave) * 64, reinterpret_cast<char*>(pk) + wave * 256);
+    }
+  };
+  if constexpr (NTRI < kWaves) prefetch_next(NTRI);
 
   // ---- per (packed P tile, lane): row r, EPL columns j; the decay
   // e^{G_r - G_j} of each v-head serves both P_rj = e^{G_r - G_j} (q_r . k_j),
@@ -1026,7 +1078,12 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
                                 16 * ln) = pack(pv);
     }
   }
-  lds_barrier();
+  // LDS writes complete, then the barrier; not lds_barrier(), whose fence
+  // would also wait for the prefetch's loads (they write LDS).  Nothing reads
+  // their scratch slots, and every wave waits for them before publishing.
+  lds_sync();
+
+  if constexpr (NTRI >= kWaves) prefetch_next(min(NH, G));
 
   // ---- per group of NH v-heads: L, T = (I + L)^{-1}, then T diag(beta) ----
   for (int hg0 = 0; hg0 < G; hg0 += NH) {
@@ -1048,7 +1105,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     if (wave < nh) {
       invert_unit_lower64(Lt + wave * kC * kLd, lane);
     }
-    lds_barrier();
+    lds_sync();  // as above
     // T diag(beta) as A tiles (rows r, k = j); only the tiles of the lower triangle
     for (int u = tid; u < nh * NTRI * 64; u += kThreads) {
       const int i = (u >> 6) / NTRI, t = (u >> 6) % NTRI, ln = u & 63;
@@ -1085,7 +1142,6 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   // (stores are acknowledged by the L2), then one flag store.  The readers are
   // on this XCD and read through the same L2. ----
   wait_stores();
-  if (tid == 0) *next_ticket = nxt;
   __syncthreads();
   if (tid == 0) {
     int32_t* ready = ws_ptr<int32_t>(A.workspace, Lay.ready);
@@ -1601,7 +1657,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
     if (tid == 0) s_tk[1] = atomicAdd(tctr, 1);
     __syncthreads();
     for (int it = s_tk[1]; it < n_items; it = s_tk[1]) {
-      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk), tctr, &s_tk[1]);
+      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk), tctr, &s_tk[1], nk, n_items,
+                                A.kh_lo + xcc);
       ++items_done;
     }
   }
