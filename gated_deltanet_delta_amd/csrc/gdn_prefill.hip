@@ -805,9 +805,8 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   };
 
   // gate inputs of the v-head whose gates this wave computes (the last G
-  // waves, one head each: they have the fewest conv items, so the gates run
-  // while the first waves finish theirs), loaded before the conv so they
-  // arrive under it
+  // waves, one head each: they have the fewest conv items), requested before
+  // the conv's inputs, so they arrive first
   static_assert(kMaxGroup <= kWaves, "one gate head per wave");
   const int ghi = kWaves - 1 - wave;
   E a_raw{}, b_raw{};
@@ -816,6 +815,37 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     a_raw = static_cast<const E*>(A.a)[i];
     b_raw = static_cast<const E*>(A.b)[i];
   }
+
+  // ---- gates: one wave per v-head, lane = token, fixed-order inclusive scan;
+  // run while the conv's inputs are on their way ----
+  auto compute_gates = [&]() {
+    if (ghi < G) {
+      const int hi = ghi;
+      float g = 0.f, bb = 0.f;
+      if (lane < len) {
+        float a_in, b_in;
+        if constexpr (BF16) {
+          a_in = bf16_bits_to_f32(a_raw);
+          b_in = bf16_bits_to_f32(b_raw);
+        } else {
+          a_in = a_raw;
+          b_in = b_raw;
+        }
+        g = -softplus_f(a_in);
+        bb = sigmoid_f(b_in);
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float up = __shfl_up(g, off, 64);
+        if (lane >= off) g += up;
+      }
+      const float glast = __shfl(g, 63, 64);
+      gcum[hi * kC + lane] = g;
+      bet[hi * kC + lane] = bb;
+      dkf[hi * kC + lane] = __expf(glast - g);
+      egt[hi * kC + lane] = __expf(g);
+    }
+  };
 
   // ---- conv + SiLU: item = (2 channels, 16 tokens); the q | k items first
   // (outputs to LDS), then the v items of the group's heads (V straight to the
@@ -839,7 +869,10 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
           load_rows<BF16, KW>(A, c0, tq, cp, raw[k]);
         }
       }
-      if (base == 0) wait_slot();  // before the first ring store
+      if (base == 0) {
+        wait_slot();  // before the first ring store
+        compute_gates();
+      }
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         const int item = base + k * kThreads + tid;
@@ -875,33 +908,6 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     }
   }
 
-  // ---- gates: one wave per v-head, lane = token, fixed-order inclusive scan ----
-  if (ghi < G) {
-    const int hi = ghi;
-    float g = 0.f, bb = 0.f;
-    if (lane < len) {
-      float a_in, b_in;
-      if constexpr (BF16) {
-        a_in = bf16_bits_to_f32(a_raw);
-        b_in = bf16_bits_to_f32(b_raw);
-      } else {
-        a_in = a_raw;
-        b_in = b_raw;
-      }
-      g = -softplus_f(a_in);
-      bb = sigmoid_f(b_in);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float up = __shfl_up(g, off, 64);
-      if (lane >= off) g += up;
-    }
-    const float glast = __shfl(g, 63, 64);
-    gcum[hi * kC + lane] = g;
-    bet[hi * kC + lane] = bb;
-    dkf[hi * kC + lane] = __expf(glast - g);
-    egt[hi * kC + lane] = __expf(g);
-  }
   lds_barrier();
 
   // ---- L2 norm factors of q and k per token: 8 lanes per token, fixed order ----
