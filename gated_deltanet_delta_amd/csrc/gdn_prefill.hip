@@ -537,9 +537,7 @@ __device__ __forceinline__ uint4 pack_lane(F f) {
   if constexpr (BF16) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(f(2 * i))) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(f(2 * i + 1))) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(f(2 * i), f(2 * i + 1));
     return make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     return make_uint4(__float_as_uint(f(0)), __float_as_uint(f(1)), __float_as_uint(f(2)), __float_as_uint(f(3)));
@@ -934,43 +932,94 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
     }
   }
   lds_barrier();
-  auto qn = [&](int r, int d) { return qk[r * QK_LD + d] * inv[r]; };
-  auto kn = [&](int r, int d) { return qk[r * QK_LD + D + d] * inv[kC + r]; };
   auto pack = [&](const float (&v)[EPL]) { return pack_lane<BF16>([&](int e) { return v[e]; }); };
 
   // ---- packing: Q and K as A tiles (rows token, k = d) to the ring, K (hi, lo)
-  // and Q into LDS; K^T as A (rows d, k = token) to the ring; gate tiles ----
-  for (int u = tid; u < 4 * KSD * 64; u += kThreads) {
-    const int tile = u >> 6, ln = u & 63;
-    const int mt = tile / KSD, ks = tile % KSD;
-    const int row = 16 * mt + (ln & 15), g = ln >> 4;
-    float kv[EPL], qv[EPL];
+  // and Q into LDS; K^T as A (rows d, k = token) to the ring; gate tiles.
+  // Every thread reads all the conv outputs and norm factors of its units
+  // (both kinds, every round) before it packs any. ----
+  {
+    constexpr int NQA = 4 * KSD * 64, NKT = NT * KSC * 64;
+    constexpr int RQA = (NQA + kThreads - 1) / kThreads, RKT = (NKT + kThreads - 1) / kThreads;
+    float kv[RQA][EPL], qv[RQA][EPL], kq_inv[RQA][2], kt[RKT][EPL], kt_inv[RKT][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int k = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
-      kv[e] = k < D ? kn(row, k) : 0.f;
-      qv[e] = k < D ? qn(row, k) : 0.f;
+    for (int rr = 0; rr < RQA; ++rr) {
+      const int u = tid + rr * kThreads;
+      const int tile = (u >> 6) % (4 * KSD), ln = u & 63;
+      const int mt = tile / KSD, ks = tile % KSD;
+      const int row = 16 * mt + (ln & 15), g = ln >> 4;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int k = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        kv[rr][e] = k < D ? qk[row * QK_LD + D + k] : 0.f;
+        qv[rr][e] = k < D ? qk[row * QK_LD + k] : 0.f;
+      }
+      kq_inv[rr][0] = inv[row];
+      kq_inv[rr][1] = inv[kC + row];
     }
-    const uint4 qw = pack(qv), kw = pack(kv);
-    *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::QA + tile) * kTileBytes + 16 * ln) = qw;
-    *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::KA + tile) * kTileBytes + 16 * ln) = kw;
-    pk[(Sm::PK_Q * 4 * KSD + tile) * 64 + ln] = qw;
-    pk[tile * 64 + ln] = kw;
-    if constexpr (BF16) {
-      float lo_[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) lo_[e] = kv[e] - bf16_bits_to_f32(f32_to_bf16_bits(kv[e]));
-      pk[(4 * KSD + tile) * 64 + ln] = pack(lo_);
+    for (int rr = 0; rr < RKT; ++rr) {
+      const int u = tid + rr * kThreads;
+      const int tile = (u >> 6) % (NT * KSC), ln = u & 63;
+      const int dt = tile / KSC, ks = tile % KSC;
+      const int dk = 16 * dt + (ln & 15), g = ln >> 4;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int r = ks * SK + (e >> 2) * 16 + 4 * g + (e & 3);
+        kt[rr][e] = qk[r * QK_LD + D + dk];
+        kt_inv[rr][e] = inv[kC + r];
+      }
     }
-  }
-  for (int u = tid; u < NT * KSC * 64; u += kThreads) {
-    const int tile = u >> 6, ln = u & 63;
-    const int dt = tile / KSC, ks = tile % KSC;
-    const int dk = 16 * dt + (ln & 15), g = ln >> 4;
-    float kv[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) kv[e] = kn(ks * SK + (e >> 2) * 16 + 4 * g + (e & 3), dk);
-    *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::KT + tile) * kTileBytes + 16 * ln) = pack(kv);
+    for (int rr = 0; rr < RQA; ++rr) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        settle(kv[rr][e]);
+        settle(qv[rr][e]);
+      }
+      settle(kq_inv[rr][0]);
+      settle(kq_inv[rr][1]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RKT; ++rr)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        settle(kt[rr][e]);
+        settle(kt_inv[rr][e]);
+      }
+#pragma unroll
+    for (int rr = 0; rr < RQA; ++rr) {
+      const int u = tid + rr * kThreads;
+      if (u >= NQA) continue;
+      const int tile = u >> 6, ln = u & 63;
+      float kn_[EPL], qn_[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kn_[e] = kv[rr][e] * kq_inv[rr][1];
+        qn_[e] = qv[rr][e] * kq_inv[rr][0];
+      }
+      const uint4 qw = pack(qn_), kw = pack(kn_);
+      *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::QA + tile) * kTileBytes + 16 * ln) = qw;
+      *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::KA + tile) * kTileBytes + 16 * ln) = kw;
+      pk[(Sm::PK_Q * 4 * KSD + tile) * 64 + ln] = qw;
+      pk[tile * 64 + ln] = kw;
+      if constexpr (BF16) {
+        float lo_[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) lo_[e] = kn_[e] - bf16_bits_to_f32(f32_to_bf16_bits(kn_[e]));
+        pk[(4 * KSD + tile) * 64 + ln] = pack(lo_);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RKT; ++rr) {
+      const int u = tid + rr * kThreads;
+      if (u >= NKT) continue;
+      const int tile = u >> 6, ln = u & 63;
+      float kn_[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kn_[e] = kt[rr][e] * kt_inv[rr][e];
+      *reinterpret_cast<uint4*>(rb + static_cast<size_t>(Gm::KT + tile) * kTileBytes + 16 * ln) = pack(kn_);
+    }
   }
   for (int u = tid; u < G * 64; u += kThreads) {
     const int hi = u >> 6, ln = u & 63;
