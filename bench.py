@@ -503,19 +503,19 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # Inside the timed steps only the prefill is bracketed by events (each
+    # event record between two launches costs a dispatch gap of several us);
+    # decode, verify and rollback are timed on their own below.
     def step(i, rec=None):
         pl = pools[i % len(pools)]
         pl2 = pools[(i + len(pools) // 2) % len(pools)]
-        e = [ev() for _ in range(5)] if rec is not None else None
+        e = [ev() for _ in range(2)] if rec is not None else None
         if e: e[0].record(stream)
         gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err)
         if e: e[1].record(stream)
         gdn.decode_step(geom, pl, dx, da, db, cw, dslot, do, dev_err=err)
-        if e: e[2].record(stream)
         gdn.verify_k(geom, pl2, vx, va, vb, cw, vslot, snap, vo, dev_err=err)
-        if e: e[3].record(stream)
         gdn.rollback(geom, pl2, snap, vslot, vacc, dev_err=err)
-        if e: e[4].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -566,9 +566,8 @@ def main():
     ms_prefill = avg_ms(0, 1)
     ms_step = gpu_ms / args.steps
 
-    # Per-path times of the short calls, each in a loop of its own: inside a
-    # step, the interval after the prefill also holds the prefill's hand-back
-    # from its second stream.  Every call still finds a cold slot pool.
+    # Per-path times of the short calls, each in a loop of its own over the
+    # cold slot pools.
     # One event pair around n back-to-back calls: the per-call time of a
     # serving loop, inter-kernel gaps included.  (Events around each call
     # would add their own dispatch latency, several µs at these sizes.)
