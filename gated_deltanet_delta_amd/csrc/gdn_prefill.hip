@@ -848,12 +848,13 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   // ---- conv + SiLU: item = (2 channels, 16 tokens); the q | k items first
   // (outputs to LDS), then the v items of the group's heads (V straight to the
   // ring in accumulator layout).  A thread takes items tid, tid + kThreads,
-  // ...; the input rows of up to three of its items (two with fp32 inputs)
-  // are requested together before any of them is used, so the loads'
-  // latency is paid once per batch of rounds, not once per round. ----
+  // ...  With fp32 inputs the input rows of two of its items are requested
+  // together before either is used; bf16 inputs come from the L2 (the
+  // previous item requested them there), and one round at a time measured
+  // faster, with fewer registers held. ----
   {
     constexpr int NQK = 4 * D;             // 2 D channels / 2 per item x 4 quarters
-    constexpr int NB = BF16 ? 3 : 2;       // rounds whose loads are in flight together
+    constexpr int NB = BF16 ? 1 : 2;       // rounds whose loads are in flight together
     const int n_items = NQK + 2 * G * D;   // + G D v channels / 2 x 4 quarters
     auto item_c0 = [&](int item, int& tq) { return conv_item_c0<D>(item, kh, Hk, G, tq); };
     for (int base = 0; base < n_items; base += NB * kThreads) {
