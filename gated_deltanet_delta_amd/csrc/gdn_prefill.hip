@@ -746,19 +746,21 @@ struct SmemBytes {
 };
 
 // The workgroup's next ticket is taken from tctr at the start and left in
-// *next_ticket (LDS) half-way, so no round trip separates one item from the
-// next, and the next item's conv inputs are requested while this one inverts.
-// A ticket t < n_tickets is item (t / nk, kh_base + 8 (t % nk)).
+// *next_ticket (LDS) half-way, as the item it names (ticket + t_off), so no
+// round trip separates one item from the next, and the next item's conv
+// inputs are requested while this one inverts.  Item i < n_tickets is
+// (chunk i / nk, k-head kh_base + 8 (i % nk)).  With tctr null no ticket is
+// taken and n_tickets is left there (an item done on its own).
 template <int D, bool BF16, int KW, int NCG>
 __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb, int chunk, int kh,
-                        int32_t* tctr, int* next_ticket, int nk, int n_tickets, int kh_base) {
+                        int32_t* tctr, int* next_ticket, int nk, int n_tickets, int kh_base, int t_off) {
   using P = Pk<BF16>;
   using Gm = Geo<D, BF16>;
   using Sm = ProdSmem<D, BF16>;
   using Ch = Chain<BF16>;
   using Bop = typename Ch::Bop;
   using E = typename P::E;
-  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, TPS = Gm::TPS, SK = P::SK, EPL = P::EPL, NT = Gm::NT;
+  constexpr int KSD = Gm::KSD, KSC = Gm::KSC, SK = P::SK, EPL = P::EPL, NT = Gm::NT;
   constexpr int NH = Sm::NH, QK_LD = Sm::QK_LD, NTRI = Gm::NTRI;
   float* smem = reinterpret_cast<float*>(sb);
   float* qk = smem;                                        // [64][QK_LD] conv outputs of q | k
@@ -776,8 +778,8 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   const int Hk = A.Hk, Hv = A.Hv, G = Hv / Hk;
   const int RS = Lay.ring_slots;
   int32_t* hdr = ws_ptr<int32_t>(A.workspace, Lay.hdr);
-  int32_t nxt = 0;
-  if (tid == 0) nxt = atomicAdd(tctr, 1);
+  int32_t nxt = n_tickets;
+  if (tid == 0 && tctr != nullptr) nxt = atomicAdd(tctr, 1) + t_off;
   const ChunkPos cp = item_pos(A, Lay, chunk);
   const int t0 = cp.t0, len = cp.len;
   char* rb = static_cast<char*>(A.workspace) + Lay.ring +
@@ -1348,7 +1350,6 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
   // ================= compute waves =================
   const int wl0 = wave * CT;       // first d_v tile of this wave within the workgroup's (V region, O slice)
   const int dvt0 = cg * NTG + wl0;  // first 16-row tile of d_v
-  const size_t rowstride = static_cast<size_t>(Hv) * D;
   int c = 0;
   for (int s = 0; s < S; ++s) {
     const int32_t* se = stab + 8 * s;
@@ -1700,23 +1701,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
   const int n_chain = nk * G * NCG;  // chains of this XCD: (k-head, v-head, column group)
   const int total = ws_ptr<int32_t>(A.workspace, L.hdr)[HDR_TOTAL];
   int chain_done = 0, items_done = 0;
-  if (ticket < n_chain) {
+  // Items of this XCD in chunk order.  A chain has nothing to do until chunk 0
+  // is ready, so chain workgroup r first produces item r; the other
+  // workgroups take items n_chain and up by ticket.  Item r < nk G NCG lies in
+  // chunk r / nk < G NCG <= the ring depth (or the call has fewer chunks than
+  // slots), so it never waits for a ring slot, which would need every chain of
+  // its k-head, this one included, to have staged an earlier chunk.
+  static_assert(kMaxGroup * NCG <= kRingSlots, "a chain's own item lies below the ring depth");
+  const int n_items = total * nk;
+  const bool is_chain = ticket < n_chain;
+  int32_t* tctr = ctr + (kXcd + xcc) * kLine;
+  if (nk > 0) {
+    __syncthreads();  // s_tk is free
+    if (tid == 0 && !is_chain) s_tk[1] = atomicAdd(tctr, 1) + n_chain;
+    __syncthreads();
+    for (int it = is_chain ? ticket : s_tk[1]; it < n_items; it = s_tk[1]) {
+      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk), is_chain ? nullptr : tctr,
+                                &s_tk[1], nk, n_items, A.kh_lo + xcc, n_chain);
+      ++items_done;
+      if (is_chain) break;
+    }
+  }
+  if (is_chain) {
     const int kh = A.kh_lo + xcc + kXcd * (ticket / (G * NCG));
     const int r = ticket % (G * NCG);
     chain_role<D, BF16, KW, CKPT, NCG>(A, L, smem, kh, kh * G + r / NCG, r % NCG);
     chain_done = 1;
-  } else if (nk > 0) {
-    // Items of this XCD in chunk order; each item takes the next ticket.
-    const int n_items = total * nk;
-    int32_t* tctr = ctr + (kXcd + xcc) * kLine;
-    __syncthreads();  // s_tk is free
-    if (tid == 0) s_tk[1] = atomicAdd(tctr, 1);
-    __syncthreads();
-    for (int it = s_tk[1]; it < n_items; it = s_tk[1]) {
-      produce<D, BF16, KW, NCG>(A, L, smem, it / nk, A.kh_lo + xcc + kXcd * (it % nk), tctr, &s_tk[1], nk, n_items,
-                                A.kh_lo + xcc);
-      ++items_done;
-    }
   }
   // Last workgroup out: every chain role and every item must have been done.
   __syncthreads();
