@@ -1254,8 +1254,9 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     // chunk c+2, which also waits for its own loads of chunk c+1.
     // The buffer refilled holds, in its V region, the output of the chunk
     // NBUF before (written there by the compute waves): each helper wave
-    // first reads the pieces of it that lie in the tiles it then overwrites
-    // itself, and stores them to o.
+    // requests the tiles outside the V region first, then reads the pieces of
+    // that output that lie in the V tiles it overwrites itself, requests
+    // those tiles and stores the pieces to o.
     constexpr int NCP = (Gm::STAGE_TILES + NHW - 1) / NHW;  // tiles loaded per helper wave
     constexpr int RW = CT * 16;            // d_v per compute wave's slice
     constexpr int VT0 = Gm::HEAD0 + Gm::HV;  // first tile of the V region
@@ -1289,7 +1290,9 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     auto poll = [&](int c) {
       wait_at_least(ready + ((c % RS) * Hk + kh) * kLine, c + 1, hdr + HDR_ABORT, A.dev_err);
     };
-    auto fill = [&](int c) {  // chunk c's tiles, ring slot c % RS, into buf(c)
+    // chunk c's tiles, ring slot c % RS, into buf(c): the tiles before the V
+    // region (v_part false) or those of the V region (true)
+    auto fill = [&](int c, bool v_part) {
       const char* rb = ringb + (static_cast<size_t>(c % RS) * Hk + kh) * Lay.item_bytes;
       char* b = buf(c);
 #pragma unroll
@@ -1297,7 +1300,8 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
         const int t = hw + j * NHW;
         const int src = t < Gm::HEAD0 ? t
                                       : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0) + (t >= VT0 ? cg * Gm::NVG : 0);
-        if (t < Gm::STAGE_TILES) load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane), b + static_cast<size_t>(t) * kTileBytes);
+        if (t < Gm::STAGE_TILES && (t >= VT0) == v_part)
+          load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane), b + static_cast<size_t>(t) * kTileBytes);
       }
     };
     // the walk as a cursor: token offset and length of the next chunk
@@ -1316,7 +1320,8 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     int prev_tok = 0, prev_len = 0;  // chunk c-1
     if (total > 0) {
       poll(0);
-      fill(0);
+      fill(0, false);
+      fill(0, true);
     }
     for (int c = 0; c < total; ++c) {
       advance();
@@ -1327,15 +1332,19 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       if (hw == 0 && lane == 0)
         __hip_atomic_store(consumed + (h * NCG + cg) * kLine, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (NBUF == 2) {
+        // the tiles outside the V region first: only the V region holds
+        // output still to be read
+        if (c + 1 < total) fill(c + 1, false);
         const Pieces ov = read_out(c - 1 < 0 ? 0 : c - 1);
-        if (c + 1 < total) fill(c + 1);
+        if (c + 1 < total) fill(c + 1, true);
         if (c >= 1) write_out(prev_tok, prev_len, ov);
       } else {
         lds_sync();  // the compute waves are done with the buffer
         const Pieces ov = read_out(c);
         if (c + 1 < total) {
           poll(c + 1);
-          fill(c + 1);
+          fill(c + 1, false);
+          fill(c + 1, true);
         }
         write_out(tok, len, ov);
       }
