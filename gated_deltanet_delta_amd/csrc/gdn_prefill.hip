@@ -942,8 +942,10 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   // Every thread reads all the conv outputs and norm factors of its units
   // (both kinds, every round) before it packs any. ----
   {
-    constexpr int NQA = 4 * KSD * 64, NKT = NT * KSC * 64;
-    constexpr int RQA = (NQA + kThreads - 1) / kThreads, RKT = (NKT + kThreads - 1) / kThreads;
+    // (K^T tiles only for fp32 inputs: the bf16 chain reads K^T from the K
+    // tiles with transposing LDS reads)
+    constexpr int NQA = 4 * KSD * 64, NKT = BF16 ? 0 : NT * KSC * 64;
+    constexpr int RQA = (NQA + kThreads - 1) / kThreads, RKT = BF16 ? 1 : (NKT + kThreads - 1) / kThreads;
     float kv[RQA][EPL], qv[RQA][EPL], kq_inv[RQA][2], kt[RKT][EPL], kt_inv[RKT][EPL];
 #pragma unroll
     for (int rr = 0; rr < RQA; ++rr) {
@@ -961,7 +963,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       kq_inv[rr][1] = inv[kC + row];
     }
 #pragma unroll
-    for (int rr = 0; rr < RKT; ++rr) {
+    for (int rr = 0; rr < (BF16 ? 0 : RKT); ++rr) {
       const int u = tid + rr * kThreads;
       const int tile = (u >> 6) % (NT * KSC), ln = u & 63;
       const int dt = tile / KSC, ks = tile % KSC;
@@ -984,7 +986,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       settle(kq_inv[rr][1]);
     }
 #pragma unroll
-    for (int rr = 0; rr < RKT; ++rr)
+    for (int rr = 0; rr < (BF16 ? 0 : RKT); ++rr)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         settle(kt[rr][e]);
@@ -1014,7 +1016,7 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < RKT; ++rr) {
+    for (int rr = 0; rr < (BF16 ? 0 : RKT); ++rr) {
       const int u = tid + rr * kThreads;
       if (u >= NKT) continue;
       const int tile = u >> 6, ln = u & 63;
@@ -1237,6 +1239,12 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
   const int32_t* stab = ws_ptr<int32_t>(A.workspace, Lay.seq_tab);
   int32_t* hdr = ws_ptr<int32_t>(A.workspace, Lay.hdr);
   auto buf = [&](int c) { return sb + static_cast<size_t>(NBUF == 2 ? (c & 1) : 0) * Gm::STAGE_BYTES; };
+  // bf16: the staged K tiles hold lane L's 16 bytes in slot k_slot(L) (an
+  // involution that keeps every 16 consecutive lanes together), so that the
+  // 16 rows a transposing read of K^T takes in one 16-lane group (lanes
+  // 4 g + m + 16 q, m, q < 4) lie in 16 different slots modulo 16, i.e. in
+  // different LDS banks; the K products read slot k_slot(lane).
+  auto k_slot = [](int L) { return L ^ (4 * ((L >> 4) & 3)); };
 
   if (wave >= NWC) {
     // ================= helper waves =================
@@ -1300,8 +1308,11 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
         const int t = hw + j * NHW;
         const int src = t < Gm::HEAD0 ? t
                                       : Gm::HEAD0 + hi * Gm::HEAD_TILES + (t - Gm::HEAD0) + (t >= VT0 ? cg * Gm::NVG : 0);
-        if (t < Gm::STAGE_TILES && (t >= VT0) == v_part)
-          load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * lane), b + static_cast<size_t>(t) * kTileBytes);
+        const bool kt_tile = BF16 && t >= Gm::KT && t < Gm::KT + NT * KSC;  // read from the K tiles instead
+        const bool k_tile = BF16 && t >= Gm::KA && t < Gm::KA + 4 * KSD;
+        if (t < Gm::STAGE_TILES && (t >= VT0) == v_part && !kt_tile)
+          load_l2_to_lds(rb, static_cast<uint32_t>(src * kTileBytes + 16 * (k_tile ? k_slot(lane) : lane)),
+                         b + static_cast<size_t>(t) * kTileBytes);
       }
     };
     // the walk as a cursor: token offset and length of the next chunk
@@ -1403,6 +1414,32 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       const float* gt = reinterpret_cast<const float*>(base + (Gm::HEAD0 + Gm::HG) * kTileBytes);
       const E* vb = reinterpret_cast<const E*>(base + Gm::V_OFF);
       auto tile = [&](const uint4* arr, int t) { return arr[t * 64 + lane]; };
+      // K^T as an A tile (rows d 16 dt.., k = tokens 32 ks..).  fp32: staged.
+      // bf16: from the K tiles (rows token, k = d) with two transposing LDS
+      // reads.  In each 16-lane group such a read hands lane j, as value m,
+      // element j % 4 of the 8 bytes lane 4 m + j / 4 addresses; so lane
+      // l = 16 g + s addresses, for read h, the four d values 16 dt + 4 (s % 4)
+      // .. +3 of token 32 ks + 16 h + 4 g + s / 4, which the K tile of token
+      // block 2 ks + h and d block dt / 2 holds in lane 4 g + s / 4 + 16 (s % 4),
+      // elements 4 (dt % 2) .. +3 (LDS slot k_slot of that lane).  Lane l then
+      // holds d = 16 dt + s and tokens 32 ks + 16 h + 4 g + m, the A layout.
+      auto kt_tile = [&](int dt, int ks) -> uint4 {
+        if constexpr (BF16) {
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const int kl = k_slot(4 * (lane >> 4) + ((lane & 15) >> 2) + 16 * (lane & 3));
+          uint2 w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const char* p = reinterpret_cast<const char*>(ka) +
+                            static_cast<size_t>((2 * ks + h) * KSD + (dt >> 1)) * kTileBytes + 16 * kl + 8 * (dt & 1);
+            w[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (__attribute__((address_space(3))) v4i16*)(p)));
+          }
+          return make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
+        } else {
+          return tile(kt, dt * KSC + ks);
+        }
+      };
 
       // The step is ordered so that VALU work independent of the MFMAs in
       // flight is issued while they run: Y = K S^T and O^T = S Q^T back to
@@ -1431,16 +1468,16 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
       // acc[ct][mt] += A(mt, ks) S^T(ks) over ks (TR: the transposed product,
       // acc[ct][mt] += S(ks) A(mt, ks)^T, rows d_v and columns token): the
       // A tiles of one ks read ahead
-      auto times_S = [&](const uint4* arr, f32x4_t (&acc)[CT][4], auto tr) {
+      auto times_S = [&](const uint4* arr, f32x4_t (&acc)[CT][4], auto tr, int ln) {
         constexpr bool TR = decltype(tr)::value;
         uint4 cur[4], nxt[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) cur[mt] = tile(arr, mt * KSD);
+        for (int mt = 0; mt < 4; ++mt) cur[mt] = arr[(mt * KSD) * 64 + ln];
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           if (ks + 1 < KSD) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) nxt[mt] = tile(arr, mt * KSD + ks + 1);
+            for (int mt = 0; mt < 4; ++mt) nxt[mt] = arr[(mt * KSD + ks + 1) * 64 + ln];
           }
           fence();
 #pragma unroll
@@ -1467,7 +1504,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           Y[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           O[ct][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-      times_S(ka, Y, std::false_type{});
+      times_S(ka, Y, std::false_type{}, BF16 ? k_slot(lane) : lane);
       // V and e^G, read under the O^T products
       using VRaw = typename std::conditional<BF16, uint2, float4>::type;
       VRaw vr[CT][4];
@@ -1479,7 +1516,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
           vr[ct][mt] = *reinterpret_cast<const VRaw*>(vb + (((wl0 + ct) * 4 + mt) * 64 + lane) * 4);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) egv[mt] = gvec(Gm::G_EG, mt);
-      times_S(qa, O, std::true_type{});
+      times_S(qa, O, std::true_type{}, lane);
       // Z = V - diag(e^G) Y as B operands of the T product
       Bop bZ[CT][KSC];
 #pragma unroll
@@ -1558,7 +1595,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
-          for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = tile(kt, i * KSC + ks);
+          for (int ks = 0; ks < KSC; ++ks) ktt[i][ks] = kt_tile(i, ks);
       };
       if constexpr (!CKPT) load_ktt();
       fence();
@@ -1623,7 +1660,7 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
             for (int i = 0; i < NT; ++i) {
               f32x4_t a = st[ct][i] * eGr;
 #pragma unroll
-              for (int ks = 0; ks < KSC; ++ks) a = Ch::step(tile(kt, i * KSC + ks), bR[ks], a);
+              for (int ks = 0; ks < KSC; ++ks) a = Ch::step(kt_tile(i, ks), bR[ks], a);
               *reinterpret_cast<float4*>(cdst + static_cast<size_t>(16 * (dvt0 + ct) + col) * D + 16 * i + 4 * g) =
                   make_float4(a[0], a[1], a[2], a[3]);
             }
