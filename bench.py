@@ -11,8 +11,10 @@ finds its state in the 256 MB last-level cache left by an earlier call.
 
 Output: one JSON line.  `value` is prefill tokens per second over whole steps
 (T tokens per step, decode and verify included in the step time).  Extra keys
-give per-path figures measured with HIP events on the launch stream: prefill
-alone (inside the steps), and decode, verify and rollback each as the device
+give per-path figures measured with HIP events on the launch stream: the
+prefill's kernels inside the steps (events recorded by the kernel launches
+themselves, gdn_prefill_timing_events, so the steps carry no event packets), and
+decode, verify and rollback each as the device
 time per call of a captured HIP graph of back-to-back calls over cold pools
 (the time of the same calls dispatched one by one from Python, which is bound
 by the host at these sizes, is reported beside it), with their GB/s and
@@ -503,21 +505,25 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # Inside the timed steps only the prefill is bracketed by events (each
-    # event record between two launches costs a dispatch gap of several us);
-    # decode, verify and rollback are timed on their own below.
-    def step(i, rec=None):
+    # Inside the timed steps the prefill's kernels are timed by events that
+    # their launches record themselves (an event record of its own between two
+    # launches would cost a dispatch gap of several us in every step); decode,
+    # verify and rollback are timed on their own below.
+    def kernel_events():
+        e = [ev() for _ in range(2)]
+        for x in e:
+            x.record(stream)  # creates the HIP event the launch will record
+        return e
+
+    def step(i, kev=None):
         pl = pools[i % len(pools)]
         pl2 = pools[(i + len(pools) // 2) % len(pools)]
-        e = [ev() for _ in range(2)] if rec is not None else None
-        if e: e[0].record(stream)
+        if kev is not None:
+            gdn.prefill_timing_events(*kev)
         gdn.prefill_chunked(geom, ppool, xp, ap, bp, cw, cu, pslot, phas, po, ws, dev_err=err)
-        if e: e[1].record(stream)
         gdn.decode_step(geom, pl, dx, da, db, cw, dslot, do, dev_err=err)
         gdn.verify_k(geom, pl2, vx, va, vb, cw, vslot, snap, vo, dev_err=err)
         gdn.rollback(geom, pl2, snap, vslot, vacc, dev_err=err)
-        if rec is not None:
-            rec.append(e)
 
     # ---------------- warmup + validity gate ----------------
     for i in range(args.warmup):
@@ -545,13 +551,13 @@ def main():
         sys.exit(4)
 
     # ---------------- timed region ----------------
-    rec = []
+    rec = [kernel_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start, e_end = ev(), ev()
     e_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, rec)
+        step(args.warmup + i, rec[i])
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -854,7 +860,8 @@ def main():
                    "n_k_heads": 16, "n_v_heads": 48, "d_k": 128, "d_v": 128, "conv_width": 4,
                    "chunk": 64, "seq_len": T_PREFILL, "decode_slots": 4, "verify_k": 4,
                    "state_dtype": "f32", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "gdn_prefill_chunked (one call: plan_kernel + prefill_kernel)",
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel of gdn_prefill_chunked, from the completion of the "
+                                               "plan_kernel before it to its own (events the launches record)",
                      "achieved": round(prefill_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic()},
         "prefill": {"ms": round(ms_prefill, 4), "tokens_per_s": round(T_PREFILL / (ms_prefill * 1e-3), 1),

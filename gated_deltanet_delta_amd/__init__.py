@@ -26,7 +26,7 @@ POS_ONE = 65536
 POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
-ABI_VERSION = 5  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
+ABI_VERSION = 6  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
 DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
@@ -88,6 +88,7 @@ _SIGS = {
     "gdn_verify_k_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
                                           _P, _P, _P, _P, _P]),
     "gdn_commit_slots": (ctypes.c_int, [ctypes.POINTER(GdnGeometry), _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "gdn_prefill_timing_events": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -398,6 +399,22 @@ def prefill_chunked(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens,
                                      _ptr(pool.conv_pos), _ptr(x), _ptr(a), _ptr(b), _ptr(conv_w),
                                      _ptr(cu_seqlens), _ptr(slot), _ptr(has_init), S, N, CHUNK,
                                      _ptr(workspace), nbytes, _ptr(o), _ptr(dev_err), _stream(stream)))
+
+
+def prefill_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]):
+    """gdn_prefill_timing_events: this thread's next prefill call records
+    ``start`` when its plan kernel completes (its main kernel begins) and
+    ``stop`` when its main kernel completes (timing events, recorded once
+    before so that they exist), through the kernel launches themselves; both
+    None clears it."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("prefill_timing_events: the event has no HIP event yet (record it once first)")
+        return h
+    _check(lib().gdn_prefill_timing_events(handle(start), handle(stop)))
 
 
 def prefill_chunked_static(geom: Geometry, pool: SlotPool, x, a, b, conv_w, cu_seqlens, slot, has_init, o,

@@ -19,6 +19,18 @@
 namespace {
 
 thread_local std::string g_last_error;
+// kernel-timing events of this thread's next prefill call (gdn_prefill_timing_events)
+thread_local void* g_prefill_ev[2] = {nullptr, nullptr};
+struct PrefillEvents {
+  void* start;
+  void* stop;
+};
+// A pending timing request, taken by the prefill call that begins now.
+PrefillEvents take_prefill_events() {
+  const PrefillEvents ev{g_prefill_ev[0], g_prefill_ev[1]};
+  g_prefill_ev[0] = g_prefill_ev[1] = nullptr;
+  return ev;
+}
 
 gdn_status fail(gdn_status s, const char* fmt, ...) {
   char buf[512];
@@ -148,7 +160,8 @@ static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_
                                const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
                                int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
-                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name);
+                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name,
+                               const PrefillEvents& ev);
 
 extern "C" {
 
@@ -167,6 +180,15 @@ const char* gdn_status_string(gdn_status s) {
 }
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_prefill_timing_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(GDN_ERR_NULL, "gdn_prefill_timing_events: %s is null, required: both events or neither",
+                start == nullptr ? "start" : "stop");
+  g_prefill_ev[0] = start;
+  g_prefill_ev[1] = stop;
+  return GDN_OK;
+}
 
 const char* gdn_version(void) { return "gdn-mi355x 0.2 (gfx950)"; }
 
@@ -382,9 +404,10 @@ gdn_status gdn_prefill_chunked(const gdn_geometry* g, float* state, float* conv_
                                const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
                                int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                size_t workspace_bytes, void* o, int32_t* dev_err, void* stream) {
+  const PrefillEvents ev = take_prefill_events();
   return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
                       n_tokens, chunk, workspace, workspace_bytes, o, 0, nullptr, 0, dev_err, stream,
-                      "gdn_prefill_chunked");
+                      "gdn_prefill_chunked", ev);
 }
 
 gdn_status gdn_prefill_chunked_static(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
@@ -393,6 +416,7 @@ gdn_status gdn_prefill_chunked_static(const gdn_geometry* g, float* state, float
                                       int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* o, int32_t* dev_err,
                                       void* stream) {
   const char* name = "gdn_prefill_chunked_static";
+  const PrefillEvents ev = take_prefill_events();
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   const size_t need = gdn_prefill_workspace_bytes(g, n_tokens, n_seqs);
@@ -406,7 +430,7 @@ gdn_status gdn_prefill_chunked_static(const gdn_geometry* g, float* state, float
   if (e != 0) return fail(GDN_ERR_LAUNCH, "%s: static workspace address not available (HIP error %d)", name, e);
   return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
                       n_tokens, chunk, ws, GDN_PREFILL_STATIC_WORKSPACE_BYTES, o, 0, nullptr, 0, dev_err, stream,
-                      name);
+                      name, ev);
 }
 
 gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* conv_state, int32_t* conv_pos,
@@ -415,11 +439,12 @@ gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* 
                                     int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                     size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
                                     size_t ckpt_bytes, int32_t* dev_err, void* stream) {
+  const PrefillEvents ev = take_prefill_events();
   if (ckpt_every <= 0)
     return fail(GDN_ERR_RANGE, "ckpt_every: %d, required: > 0", ckpt_every);
   return prefill_call(g, state, conv_state, conv_pos, x, a_in, b_in, conv_w, cu_seqlens, slot, has_init, n_seqs,
                       n_tokens, chunk, workspace, workspace_bytes, o, ckpt_every, ckpt, ckpt_bytes, dev_err,
-                      stream, "gdn_prefill_chunked_ckpt");
+                      stream, "gdn_prefill_chunked_ckpt", ev);
 }
 
 }  // extern "C"
@@ -430,7 +455,8 @@ static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_
                                const int32_t* cu_seqlens, const int32_t* slot, const int32_t* has_init,
                                int32_t n_seqs, int32_t n_tokens, int32_t chunk, void* workspace,
                                size_t workspace_bytes, void* o, int32_t ckpt_every, float* ckpt,
-                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name) {
+                               size_t ckpt_bytes, int32_t* dev_err, void* stream, const char* name,
+                               const PrefillEvents& ev) {
   gdn_status s = check_geometry(g);
   if (s != GDN_OK) return s;
   if (chunk != gdn::kChunk)
@@ -497,5 +523,5 @@ static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_
     a.ckpt = ckpt;
     a.ckpt_every = ckpt_every;
   }
-  return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream), name);
+  return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream, ev.start, ev.stop), name);
 }

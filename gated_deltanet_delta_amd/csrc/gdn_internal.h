@@ -114,7 +114,10 @@ int launch_verify(const StepArgs& a, bool bf16, void* stream);
 int launch_conv_step(const StepArgs& a, bool bf16, void* stream);
 int launch_rollback(const StepArgs& a, void* stream);
 int launch_commit_slots(const StepArgs& a, void* stream);
-int launch_prefill(const PrefillArgs& a, bool bf16, void* stream);
+// ev_start / ev_stop (hipEvent_t, optional): recorded by the call's kernel
+// launches themselves, when the plan kernel ends (the main kernel begins) and
+// when the last main kernel ends.
+int launch_prefill(const PrefillArgs& a, bool bf16, void* stream, void* ev_start = nullptr, void* ev_stop = nullptr);
 // Device address of the library's static prefill workspace on the GPU of
 // `stream` (GDN_PREFILL_STATIC_WORKSPACE_BYTES); a HIP error code, 0 on success.
 int prefill_static_workspace(void* stream, void** ptr);

@@ -65,6 +65,8 @@
 
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -1795,12 +1797,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs A, Pre
 // Launcher
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st) {
+static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const PrefillLayout L = layout_t<D, BF16>(a0.Hk, a0.Hv, a0.n_tokens, a0.n_seqs);
   const int ncg = ncg_of<D, BF16>();
   const int n_launch = launches(a0.Hk, a0.Hv, ncg);
   const int per = heads_per_launch(a0.Hk, a0.Hv, ncg);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L, n_launch);
+  if (ev_start != nullptr || ev_stop != nullptr) {
+    // an event recorded under capture would not time anything: refuse
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(st, &cs);
+    if (ce != hipSuccess) return static_cast<int>(ce);
+    if (cs != hipStreamCaptureStatusNone) return static_cast<int>(hipErrorStreamCaptureUnsupported);
+  }
+  // `start` is the plan kernel's completion, where the main kernel begins (a
+  // launch's start event can be stamped before the previous kernel is done)
+  if (ev_start != nullptr)
+    hipExtLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, nullptr, ev_start, 0, a0, L, n_launch);
+  else
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a0, L, n_launch);
   int e = static_cast<int>(hipGetLastError());
   if (e) return e;
   auto fn = a0.ckpt_every > 0 ? (a0.W == 4 ? &prefill_kernel<D, BF16, 4, true> : &prefill_kernel<D, BF16, 0, true>)
@@ -1811,7 +1825,11 @@ static int launch_prefill_t(const PrefillArgs& a0, hipStream_t st) {
     a.kh_hi = a.kh_lo + per < a0.Hk ? a.kh_lo + per : a0.Hk;
     a.seg = seg;
     a.last_seg = seg == n_launch - 1;
-    hipLaunchKernelGGL(fn, dim3(kXcd * kWgPerXcd), dim3(kThreads), 0, st, a, L);
+    hipEvent_t ee = seg == n_launch - 1 ? ev_stop : nullptr;
+    if (ee != nullptr)
+      hipExtLaunchKernelGGL(fn, dim3(kXcd * kWgPerXcd), dim3(kThreads), 0, st, nullptr, ee, 0, a, L);
+    else
+      hipLaunchKernelGGL(fn, dim3(kXcd * kWgPerXcd), dim3(kThreads), 0, st, a, L);
     e = static_cast<int>(hipGetLastError());
     if (e) return e;
   }
@@ -1855,14 +1873,15 @@ int prefill_static_workspace(void* stream, void** ptr) {
   return 0;
 }
 
-int launch_prefill(const PrefillArgs& a, bool bf16, void* stream) {
+int launch_prefill(const PrefillArgs& a, bool bf16, void* stream, void* ev_start, void* ev_stop) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   switch (a.D) {
-    case 16: return bf16 ? launch_prefill_t<16, true>(a, s) : launch_prefill_t<16, false>(a, s);
-    case 32: return bf16 ? launch_prefill_t<32, true>(a, s) : launch_prefill_t<32, false>(a, s);
-    case 64: return bf16 ? launch_prefill_t<64, true>(a, s) : launch_prefill_t<64, false>(a, s);
+    case 16: return bf16 ? launch_prefill_t<16, true>(a, s, e0, e1) : launch_prefill_t<16, false>(a, s, e0, e1);
+    case 32: return bf16 ? launch_prefill_t<32, true>(a, s, e0, e1) : launch_prefill_t<32, false>(a, s, e0, e1);
+    case 64: return bf16 ? launch_prefill_t<64, true>(a, s, e0, e1) : launch_prefill_t<64, false>(a, s, e0, e1);
     case 128:
-      if (bf16) return launch_prefill_t<128, true>(a, s);
+      if (bf16) return launch_prefill_t<128, true>(a, s, e0, e1);
       return static_cast<int>(hipErrorInvalidValue);  // refused by the API before any launch
     default: return static_cast<int>(hipErrorInvalidValue);
   }

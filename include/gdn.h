@@ -82,9 +82,10 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
+#define GDN_ABI_VERSION 6  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
                               checkpoints at any block size, GDN_DEV_INCOMPLETE;
-                              5: gdn_prefill_chunked_static */
+                              5: gdn_prefill_chunked_static;
+                              6: gdn_prefill_timing_events */
 /* bytes of the library's own prefill workspace, one per GPU (gdn_prefill_chunked_static) */
 #define GDN_PREFILL_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
 #define GDN_POS_ONE 65536
@@ -293,6 +294,26 @@ gdn_status gdn_prefill_chunked_ckpt(const gdn_geometry* g, float* state, float* 
                                     size_t workspace_bytes, void* o, int32_t ckpt_every,
                                     float* ckpt, size_t ckpt_bytes, int32_t* dev_err,
                                     void* stream);
+
+/*
+ * Kernel timing, for measurement: the next gdn_prefill_chunked,
+ * gdn_prefill_chunked_static or gdn_prefill_chunked_ckpt call made on this
+ * host thread records `start` when its small plan kernel completes, which is
+ * where its main kernel begins, and `stop` when its last main kernel
+ * completes, through the kernel launches themselves (hipExtLaunchKernel), so
+ * no event packet is put between the call's kernels and the caller's.  The
+ * interval is the main kernel's run (the plan kernel, about 4 us, precedes
+ * it).  `start` and `stop` are hipEvent_t handles the caller created
+ * beforehand and still owns.  The
+ * request is consumed by that next prefill call, whatever its outcome; both
+ * null clears it.  A prefill under graph capture with a request pending fails
+ * with GDN_ERR_LAUNCH and launches nothing: an event recorded under capture
+ * times nothing, and a measurement that would read as zero must refuse
+ * ("Chapter 6: engine startup and memory plan", section 6.10, on the
+ * stage-timing guard).  Host only, thread-local, launches nothing.
+ * Errors: GDN_ERR_NULL when exactly one of the two is null.
+ */
+gdn_status gdn_prefill_timing_events(void* start, void* stop);
 
 /*
  * Speculative verify of k draft tokens per batch row ("Forge", 27 August:

@@ -125,6 +125,13 @@ int main(void) {
   g.dtype_in = g.dtype_out = GDN_F32;
   CHECK(48, gdn_prefill_chunked(&g, PF, PF, PI, P, P, P, PF, PI, PI, PI, 1, 8192, 64, P, w1, P, NULL, NULL) ==
                 GDN_ERR_UNSUPPORTED);
+  /* kernel-timing requests: both events or neither; consumed by the next prefill call */
+  CHECK(60, gdn_prefill_timing_events(P, NULL) == GDN_ERR_NULL && has("stop is null"));
+  CHECK(61, gdn_prefill_timing_events(NULL, P) == GDN_ERR_NULL);
+  CHECK(62, gdn_prefill_timing_events(P, P) == GDN_OK);
+  CHECK(63, gdn_prefill_chunked(&g, PF, PF, PI, P, P, P, PF, PI, PI, PI, 1, 8192, 128, P, w1, P, NULL, NULL) ==
+                GDN_ERR_UNSUPPORTED);
+  CHECK(64, gdn_prefill_timing_events(NULL, NULL) == GDN_OK);
   /* strings */
   for (int s = -1; s <= 8; ++s) CHECK(50, gdn_status_string((gdn_status)s) != NULL);
   CHECK(51, strcmp(gdn_status_string(GDN_ERR_WORKSPACE), "GDN_ERR_WORKSPACE") == 0);

@@ -185,6 +185,21 @@ def test_prefill_static_refusals(gdn):
     assert call() == 3
 
 
+def test_prefill_timing_events_requests(gdn):
+    """The kernel-timing request takes both events or neither, and the next
+    prefill call consumes it even when that call is refused before any launch
+    (the handles here are never used: no call below passes validation)."""
+    L = gdn.lib()
+    assert L.gdn_prefill_timing_events(_p(), None) == 1  # GDN_ERR_NULL
+    assert "stop is null" in L.gdn_last_error().decode()
+    assert L.gdn_prefill_timing_events(None, _p()) == 1
+    assert L.gdn_prefill_timing_events(_p(), _p()) == 0
+    g = _geom(gdn, n_k_heads=64, n_v_heads=192)
+    assert L.gdn_prefill_chunked_static(ctypes.byref(g), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                                        _p(), 1, 8192, 64, _p(), None, None) == 6
+    assert L.gdn_prefill_timing_events(None, None) == 0
+
+
 def test_prefill_checkpoint_refusals(gdn):
     L = gdn.lib()
     g = _geom(gdn)
