@@ -26,7 +26,7 @@ POS_ONE = 65536
 POS_STRIDE = 32  # int32 words per slot in conv_pos: slot s's position is conv_pos[s, 0]
 CHUNK = 64
 
-ABI_VERSION = 6  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
+ABI_VERSION = 7  # GDN_ABI_VERSION of include/gdn.h that these signatures follow
 DEV_OK = 0
 DEV_BAD_SLOT = 1
 DEV_BAD_ACCEPTED = 2
@@ -34,6 +34,7 @@ DEV_BAD_SEQLENS = 3
 DEV_WAIT_TIMEOUT = 4
 DEV_BAD_K = 5
 DEV_INCOMPLETE = 6
+DEV_DUP_SLOT = 7  # libgdn_debug.so only
 
 
 class GdnGeometry(ctypes.Structure):

@@ -3,6 +3,9 @@
     python -m gated_deltanet_delta_amd.build        # or: from ... import build; build.build()
 
 Objects go to <repo>/_build/, the library to gated_deltanet_delta_amd/libgdn.so.
+Beside it, libgdn_debug.so: the same kernels with the C ABI built with
+GDN_DEBUG_CHECKS (each call also checks on the device that its slot ids are
+distinct, GDN_DEV_DUP_SLOT).
 """
 from __future__ import annotations
 
@@ -18,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+LIB_DEBUG = os.path.join(PKG, "libgdn_debug.so")
 
 HIP_SOURCES = ["gdn_step.hip", "gdn_prefill.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
@@ -65,16 +69,21 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         jobs.append([hipcc, *HIPCC_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj])
+    debug_objs = list(objs)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
+        dobj = os.path.join(BUILD, src + ".debug.o")
         objs.append(obj)
+        debug_objs.append(dobj)
         jobs.append(["g++", *HOST_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["g++", *HOST_FLAGS, "-DGDN_DEBUG_CHECKS=1", *incs, "-c", os.path.join(CSRC, src), "-o", dobj])
     with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (LIB_DEBUG, debug_objs)):
+        tmp = lib + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -19,6 +19,19 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Debug builds check that a call's slot ids are distinct before its kernels.
+#ifdef GDN_DEBUG_CHECKS
+#define GDN_DEBUG_DISTINCT(name, a, na, b, nb, kb, k_row)                                               \
+  do {                                                                                                 \
+    const int e_ = gdn::launch_check_distinct(a, na, b, nb, kb, k_row, dev_err, stream);               \
+    if (e_ != 0) return fail(GDN_ERR_LAUNCH, "%s: HIP launch of the slot check failed with error %d", name, e_); \
+  } while (0)
+#else
+#define GDN_DEBUG_DISTINCT(name, a, na, b, nb, kb, k_row) \
+  do {                                                  \
+  } while (0)
+#endif
 // kernel-timing events of this thread's next prefill call (gdn_prefill_timing_events)
 thread_local void* g_prefill_ev[2] = {nullptr, nullptr};
 struct PrefillEvents {
@@ -190,7 +203,11 @@ gdn_status gdn_prefill_timing_events(void* start, void* stop) {
   return GDN_OK;
 }
 
+#ifdef GDN_DEBUG_CHECKS
+const char* gdn_version(void) { return "gdn-mi355x 0.2 (gfx950, debug checks)"; }
+#else
 const char* gdn_version(void) { return "gdn-mi355x 0.2 (gfx950)"; }
+#endif
 
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
@@ -232,6 +249,7 @@ gdn_status gdn_conv_state_step(const gdn_geometry* g, float* conv_state, int32_t
   a.dev_err = dev_err;
   a.batch = batch;
   a.k = 1;
+  GDN_DEBUG_DISTINCT("gdn_conv_state_step", slot, batch, nullptr, 0, 0, nullptr);
   return launched(gdn::launch_conv_step(a, g->dtype_in == GDN_BF16, stream), "gdn_conv_state_step");
 }
 
@@ -265,6 +283,7 @@ gdn_status gdn_decode_step(const gdn_geometry* g, float* state, float* conv_stat
   a.dev_err = dev_err;
   a.batch = batch;
   a.k = 1;
+  GDN_DEBUG_DISTINCT("gdn_decode_step", slot, batch, nullptr, 0, 0, nullptr);
   return launched(gdn::launch_decode(a, g->dtype_in == GDN_BF16, stream), "gdn_decode_step");
 }
 
@@ -303,6 +322,7 @@ gdn_status gdn_verify_k(const gdn_geometry* g, const float* state, float* conv_s
   a.dev_err = dev_err;
   a.batch = batch;
   a.k = k;
+  GDN_DEBUG_DISTINCT("gdn_verify_k", slot, batch, nullptr, 0, 0, nullptr);
   return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k");
 }
 
@@ -346,6 +366,7 @@ gdn_status gdn_verify_k_slots(const gdn_geometry* g, float* state, float* conv_s
   a.dev_err = dev_err;
   a.batch = batch;
   a.k = k;
+  GDN_DEBUG_DISTINCT("gdn_verify_k_slots", slot, batch, snap_slot, batch, k, k_row);
   return launched(gdn::launch_verify(a, g->dtype_in == GDN_BF16, stream), "gdn_verify_k_slots");
 }
 
@@ -396,6 +417,7 @@ gdn_status gdn_rollback(const gdn_geometry* g, float* state, int32_t* conv_pos, 
   a.dev_err = dev_err;
   a.batch = batch;
   a.k = k;
+  GDN_DEBUG_DISTINCT("gdn_rollback", slot, batch, nullptr, 0, 0, nullptr);
   return launched(gdn::launch_rollback(a, stream), "gdn_rollback");
 }
 
@@ -523,5 +545,6 @@ static gdn_status prefill_call(const gdn_geometry* g, float* state, float* conv_
     a.ckpt = ckpt;
     a.ckpt_every = ckpt_every;
   }
+  GDN_DEBUG_DISTINCT(name, slot, n_seqs, nullptr, 0, 0, nullptr);
   return launched(gdn::launch_prefill(a, g->dtype_in == GDN_BF16, stream, ev.start, ev.stop), name);
 }

@@ -114,6 +114,12 @@ int launch_verify(const StepArgs& a, bool bf16, void* stream);
 int launch_conv_step(const StepArgs& a, bool bf16, void* stream);
 int launch_rollback(const StepArgs& a, void* stream);
 int launch_commit_slots(const StepArgs& a, void* stream);
+// Debug builds: one small kernel reporting GDN_DEV_DUP_SLOT to *dev_err when
+// two of a call's slot ids are equal: a[0..na), then, for rows i < nb, the
+// ids b[i kb + j] for j < kb, or j < k_row[i] when k_row is given (rows whose
+// count is out of range are left out).  Nothing is launched without dev_err.
+int launch_check_distinct(const int32_t* a, int na, const int32_t* b, int nb, int kb, const int32_t* k_row,
+                          int32_t* dev_err, void* stream);
 // ev_start / ev_stop (hipEvent_t, optional): recorded by the call's kernel
 // launches themselves, when the plan kernel ends (the main kernel begins) and
 // when the last main kernel ends.

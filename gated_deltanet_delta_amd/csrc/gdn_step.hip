@@ -375,6 +375,44 @@ __global__ __launch_bounds__(256) void commit_slots_kernel(StepArgs A) {
   }
 }
 
+// Debug builds: two equal slot ids in one call (every id against every earlier one).
+__global__ __launch_bounds__(256) void distinct_slots_kernel(const int32_t* a, int na, const int32_t* b, int nb,
+                                                             int kb, const int32_t* k_row, int32_t* dev_err) {
+  const int n = na + nb * kb;
+  auto id = [&](int e, bool& used) {
+    if (e < na) {
+      used = true;
+      return a[e];
+    }
+    const int i = (e - na) / kb, j = (e - na) % kb;
+    const int kr = k_row != nullptr ? k_row[i] : kb;
+    used = kr >= 1 && kr <= kb && j < kr;
+    return used ? b[static_cast<size_t>(i) * kb + j] : 0;
+  };
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    bool ue = false;
+    const int ve = id(e, ue);
+    if (!ue) continue;
+    for (int f = 0; f < e; ++f) {
+      bool uf = false;
+      const int vf = id(f, uf);
+      if (uf && vf == ve) {
+        report_error(dev_err, GDN_DEV_DUP_SLOT);
+        break;
+      }
+    }
+  }
+}
+
+int launch_check_distinct(const int32_t* a, int na, const int32_t* b, int nb, int kb, const int32_t* k_row,
+                          int32_t* dev_err, void* stream) {
+  if (dev_err == nullptr || na + (b != nullptr ? nb * kb : 0) < 2) return 0;
+  if (b == nullptr) nb = 0;
+  hipLaunchKernelGGL(distinct_slots_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), a, na, b, nb,
+                     kb > 0 ? kb : 1, k_row, dev_err);
+  return static_cast<int>(hipGetLastError());
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------

@@ -40,7 +40,10 @@
  *    skipped: nothing is clamped, nothing is written out of range.
  *  - Buffers read or written by a call must not alias each other (x, a, b,
  *    o, snap, workspace vs state and conv_state).  Slot ids within one call
- *    must be distinct; duplicates give undefined results.
+ *    must be distinct; duplicates give undefined results.  A library built
+ *    with GDN_DEBUG_CHECKS (libgdn_debug.so) checks this on the device before
+ *    each call's kernels and writes GDN_DEV_DUP_SLOT to *dev_err (calls
+ *    without dev_err are not checked); the release library does not.
  *  - Every pointer to float data and every x / o / snap / workspace pointer
  *    must be 16-byte aligned.
  *  - Calls on one stream are ordered; calls that overlap in time on the same
@@ -82,10 +85,11 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
+#define GDN_ABI_VERSION 7  /* 4: prefill on the caller's stream alone, workspace independent of n_tokens,
                               checkpoints at any block size, GDN_DEV_INCOMPLETE;
                               5: gdn_prefill_chunked_static;
-                              6: gdn_prefill_timing_events */
+                              6: gdn_prefill_timing_events;
+                              7: GDN_DEV_DUP_SLOT (debug builds) */
 /* bytes of the library's own prefill workspace, one per GPU (gdn_prefill_chunked_static) */
 #define GDN_PREFILL_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
 #define GDN_POS_ONE 65536
@@ -110,6 +114,8 @@ typedef enum gdn_status {
 #define GDN_DEV_WAIT_TIMEOUT 4   /* prefill: a hand-off between its workgroups stalled (bounded wait); outputs invalid */
 #define GDN_DEV_BAD_K 5          /* a row's draft count outside [1, k] */
 #define GDN_DEV_INCOMPLETE 6     /* prefill: part of the work was never picked up by a workgroup; outputs invalid */
+#define GDN_DEV_DUP_SLOT 7       /* two rows of one call name the same slot; written only by a library built with
+                                    GDN_DEBUG_CHECKS (libgdn_debug.so), which checks this before each call's kernels */
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 

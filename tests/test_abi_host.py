@@ -298,3 +298,17 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         m.lib()
+
+
+def test_debug_library_builds_the_same_abi(gdn):
+    """libgdn_debug.so (the C ABI built with GDN_DEBUG_CHECKS, which checks a
+    call's slot ids on the device) exports every declared symbol of the same
+    ABI version and says so in its version string."""
+    import os
+    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_debug.so")
+    L = ctypes.CDLL(path)
+    assert [n for n in declared_functions() if not hasattr(L, n)] == []
+    L.gdn_version.restype = ctypes.c_char_p
+    L.gdn_abi_version.restype = ctypes.c_int32
+    assert b"debug checks" in L.gdn_version() and b"debug" not in gdn.lib().gdn_version()
+    assert L.gdn_abi_version() == gdn.ABI_VERSION
