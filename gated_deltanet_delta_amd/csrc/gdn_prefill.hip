@@ -22,19 +22,20 @@
 //            the XCD it runs on and takes a ticket from that XCD's counter.
 //            All the work of a k-head stays on one XCD, so everything passed
 //            between workgroups goes through that XCD's L2:
-//            - the first tickets are chain workgroups, one per v-head of the
-//              XCD's k-heads.  A chain workgroup walks every sequence's chunks
-//              in order and keeps the v-head's state S^T in MFMA accumulators
-//              from the first chunk of a sequence to its last; per chunk it
-//              does what depends on the state: K S^T, U, Q S^T, P U and the
-//              state update.  Its helper waves compute V (conv + SiLU of the
-//              v channels) and stage the next chunk's operands into LDS.
+//            - the first tickets are chain workgroups, one per (v-head, column
+//              group) of the XCD's k-heads.  A chain workgroup first produces
+//              one of the earliest items (below), then walks every sequence's
+//              chunks in order and keeps its columns of the v-head's state S^T
+//              in MFMA accumulators from the first chunk of a sequence to its
+//              last; per chunk it does what depends on the state: K S^T, U,
+//              Q S^T, P U and the state update.  Its helper waves stage the
+//              next chunk's operands into LDS and store the output.
 //            - the other workgroups are producers: they take (chunk, k-head)
 //              items in chunk order and compute what does not depend on the
-//              state -- conv + SiLU + L2 norm of q and k, the gates and their
-//              cumulative sums, K K^T and K Q^T on MFMA, then per v-head P and
-//              T diag(beta) with T = (I + L)^{-1} -- written pre-packed in MFMA
-//              operand order into a ring of chunk slots.
+//              state -- conv + SiLU of q, k and v, the L2 norms of q and k, the
+//              gates and their cumulative sums, K K^T and K Q^T on MFMA, then
+//              per v-head P and T diag(beta) with T = (I + L)^{-1} -- written
+//              pre-packed in MFMA operand order into a ring of chunk slots.
 //            A producer publishes (chunk, k-head) with a flag once its stores
 //            have reached the L2; a chain workgroup marks a chunk consumed once
 //            it sits in LDS, and a producer reuses a ring slot only after every
@@ -43,7 +44,9 @@
 // Forward progress.  A workgroup takes its ticket only while it runs, and the
 // first tickets of every XCD are the chain roles, so every chain workgroup is
 // resident before any producer exists.  Chain workgroups wait only on items
-// published by producers; a producer waits only on the chain having consumed
+// published by producers (the one item a chain workgroup produces first lies
+// in a chunk below the ring depth, so it waits for nothing); a producer
+// waits only on the chain having consumed
 // a chunk RING slots older than its own.  Items are taken in chunk order by
 // running workgroups, so the producer of the oldest unpublished item is always
 // resident and its wait is always on already published chunks: the chain can
@@ -940,7 +943,8 @@ __device__ void produce(const PrefillArgs& A, const PrefillLayout& Lay, char* sb
   auto pack = [&](const float (&v)[EPL]) { return pack_lane<BF16>([&](int e) { return v[e]; }); };
 
   // ---- packing: Q and K as A tiles (rows token, k = d) to the ring, K (hi, lo)
-  // and Q into LDS; K^T as A (rows d, k = token) to the ring; gate tiles.
+  // and Q into LDS; for fp32 inputs K^T as A (rows d, k = token) to the ring;
+  // gate tiles.
   // Every thread reads all the conv outputs and norm factors of its units
   // (both kinds, every round) before it packs any. ----
   {
@@ -1257,8 +1261,9 @@ __device__ void chain_role(const PrefillArgs& A, const PrefillLayout& Lay, char*
     // The helper waves walk the same chunks as the compute waves (every valid
     // sequence's chunks in order).  Right after chunk c's barrier the buffer
     // of chunk c+1 is free (the compute waves are done with chunk c-1): the
-    // helpers issue loads that write the item's tiles (the k-head's Q, K,
-    // K^T; this v-head's T diag(beta), P, gates and V) straight from the L2
+    // helpers issue loads that write the item's tiles (the k-head's Q and K,
+    // and K^T for fp32 inputs; this v-head's T diag(beta), P, gates and V of
+    // the workgroup's columns) straight from the L2
     // into that buffer, so they land while chunk c is computed.  Before
     // chunk c+1's barrier each helper wave polls the producer's flag for
     // chunk c+2, which also waits for its own loads of chunk c+1.
