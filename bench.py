@@ -7,7 +7,9 @@ One step = one pass of every path of the layer on synthetic inputs resident in H
   * verify of k = 4 drafts on 4 slots, then rollback to seeded accepted lengths.
 
 Decode and verify rotate through enough slot pools (32 x 24 MiB) that no call
-finds its state in the 256 MB last-level cache left by an earlier call.
+finds its state in the 256 MB last-level cache left by an earlier call; the
+run refuses unless that cold decode is clearly slower than the same calls on
+one warm pool (`decode.warm_pool_us`, `decode.cold_over_warm`).
 
 Output: one JSON line.  `value` is prefill tokens per second over whole steps
 (T tokens per step, decode and verify included in the step time).  Extra keys
@@ -59,6 +61,7 @@ ROLLBACK_BYTES_PER_SLOT = 6_291_456
 CKPT_EVERY = (512, 528)                        # tokens between state checkpoints
 DECODE_SWEEP = (16, 64, 256)                   # decode batch sizes of the sweep
 STACK_LAYERS = 36                              # GDN layers of the stack figure
+COLD_OVER_WARM_MIN = 1.05                      # cold-pool decode at least this much slower than one warm pool
 
 
 def expected_tokens(p: float, k: int) -> float:
@@ -625,6 +628,18 @@ def main():
     if int(err.item()) != 0:
         print(json.dumps({"error": f"device error code {int(err.item())} in the per-path loops"}))
         sys.exit(3)
+    # Cold-pool gate: the same 64 decode calls on one pool, whose 25 MB of
+    # state the 256 MB last-level cache keeps between calls, must be clearly
+    # faster than the rotation over the cold pools (about 6 against 7.3 us);
+    # otherwise the cold figures would be served from that cache, and the run
+    # refuses rather than print them.
+    ms_decode_warm = graph_ms(lambda i: gdn.decode_step(geom, pools[0], dx, da, db, cw, dslot, do, dev_err=err),
+                              n_loop)
+    if not ms_decode >= COLD_OVER_WARM_MIN * ms_decode_warm:
+        print(json.dumps({"error": f"cold-pool decode {ms_decode * 1e3:.2f} us is not {COLD_OVER_WARM_MIN}x the "
+                                   f"warm-pool decode {ms_decode_warm * 1e3:.2f} us: the cold protocol did not "
+                                   "keep the state out of the last-level cache"}))
+        sys.exit(6)
 
     # Variable-length batched prefill: 4 sequences with the seeded lengths of
     # the varlen workload (about 101 K tokens), one call, event-timed.
@@ -871,7 +886,8 @@ def main():
         "decode": {"us": round(ms_decode * 1e3, 2), "state_gbs": round(decode_state_gbs, 1),
                    "total_gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
                    "timing": "graph replay", "eager_loop_us": round(ms_decode_eager * 1e3, 2),
-                   "cold_pools": len(pools)},
+                   "cold_pools": len(pools), "warm_pool_us": round(ms_decode_warm * 1e3, 2),
+                   "cold_over_warm": round(ms_decode / ms_decode_warm, 3)},
         "verify": {"us": round(ms_verify * 1e3, 2), "gbs": round(verify_gbs, 1),
                    "frac_hbm_peak": round(verify_gbs / HBM_PEAK_GBS, 4),
                    "timing": "graph replay", "eager_loop_us": round(ms_verify_eager * 1e3, 2)},
