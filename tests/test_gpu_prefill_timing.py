@@ -109,3 +109,41 @@ def test_pending_request_refused_under_capture():
         for i, (a, b) in enumerate(zip(results(), ref)):
             assert torch.equal(a, b), f"replay {rep}: result {i} differs from the eager run"
         del o_junk
+
+
+def test_every_prefill_entry_point_takes_the_request():
+    """The static-workspace prefill and the prefill with checkpoints record the
+    events too (each consumes the request), with results unchanged."""
+    import gated_deltanet_delta_amd as gdn
+    gdn.lib()
+    g = dataclasses.replace(gi.GEOM_QWEN, n_k_heads=2, n_v_heads=6, n_slots=2)
+    geom = H.to_geom(g)
+    dt = H.in_dtype(g)
+    T, every = 700, 256
+    inp = gi.prefill_inputs(seed=962, geom=g, lengths=[T], init_state=True)
+    args = (H.dev(inp["x"], dt), H.dev(inp["a"], dt), H.dev(inp["b"], dt), H.dev(inp["conv_w"]),
+            H.dev(inp["cu_seqlens"]), H.dev(inp["slots"]), H.dev(inp["has_init"]))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = gdn.alloc_prefill_workspace(geom, T, 1)
+    k0, k1 = _events()
+
+    def run(kind, timed):
+        pool = H.make_pool(g, inp["state"], inp["hist"], inp["pos"])
+        o = torch.empty(T, g.n_v_heads, g.d_v, dtype=dt, device="cuda")
+        ckpt = torch.empty(T // every, g.n_v_heads, g.d_v, g.d_k, dtype=torch.float32, device="cuda")
+        if timed:
+            gdn.prefill_timing_events(k0, k1)
+        if kind == "static":
+            gdn.prefill_chunked_static(geom, pool, *args, o, dev_err=err)
+        else:
+            gdn.prefill_chunked(geom, pool, *args, o, ws, dev_err=err, ckpt=ckpt, ckpt_every=every)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        return [o, pool.state, pool.conv_state, pool.conv_pos] + ([ckpt] if kind == "ckpt" else [])
+
+    for kind in ("static", "ckpt"):
+        ref = run(kind, False)
+        got = run(kind, True)
+        assert k0.elapsed_time(k1) > 0.0, kind
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"{kind}: result {i} differs with timing events"
