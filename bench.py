@@ -62,7 +62,8 @@ ROLLBACK_BYTES_PER_SLOT = 6_291_456
 CKPT_EVERY = (512, 528)                        # tokens between state checkpoints
 DECODE_SWEEP = (16, 64, 256)                   # decode batch sizes of the sweep
 STACK_LAYERS = 36                              # GDN layers of the stack figure
-COLD_OVER_WARM_MIN = 1.05                      # cold-pool decode at least this much slower than one warm pool
+COLD_OVER_WARM_MIN = 1.10                      # cold-pool decode at least this much slower than one warm pool
+LAST_LEVEL_CACHE_BYTES = 256 << 20             # MI355X's last-level (Infinity) cache
 PREFILL_TIMING_EVERY = 4                       # the prefill kernel is timed on every 4th timed step
 
 
@@ -99,7 +100,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--pools", type=int, default=32)
+    p.add_argument("--pools", type=int, default=32,
+                   help="slot pools the decode, verify and rollback calls rotate over, so that each call finds its "
+                        "state out of the last-level cache (at least 1; too few and the cold-pool gate refuses)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-varlen", action="store_true", help="skip the variable-length prefill figure")
     p.add_argument("--no-ckpt", action="store_true", help="skip the checkpoint-prefill figure")
@@ -448,6 +451,9 @@ def main():
         print(json.dumps({"error": "this benchmark measures one GPU; the layer's multi-GPU "
                                    "sharding is a design note, not a measured path", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.pools < 1:
+        print(json.dumps({"error": f"--pools {args.pools}: at least one slot pool is needed"}))
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -464,6 +470,15 @@ def main():
     if args.pmc_probe_verify:
         pmc_probe_verify()
         return
+    # The rotation must hold more than twice the last-level cache, or a call
+    # could find its pool's state still cached from the previous round.
+    g0 = gdn.Geometry()
+    pool_bytes = g0.n_slots * g0.n_v_heads * g0.d_v * g0.d_k * 4   # fp32 states of one pool
+    if args.pools * pool_bytes <= 2 * LAST_LEVEL_CACHE_BYTES:
+        print(json.dumps({"error": f"--pools {args.pools}: {args.pools} x {pool_bytes} state bytes do not exceed twice "
+                                   f"the {LAST_LEVEL_CACHE_BYTES >> 20} MiB last-level cache, so the decode, verify and "
+                                   "rollback figures would not be cold"}))
+        sys.exit(6)
     gdn.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -621,7 +636,9 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (n * reps)
 
-    n_loop = 2 * len(pools)
+    # calls per captured graph: at least 64 whatever the pool count, so a
+    # replay's own launch cost stays small against the calls it holds
+    n_loop = max(64, 2 * len(pools))
     f_decode = lambda i: gdn.decode_step(geom, pools[i % len(pools)], dx, da, db, cw, dslot, do, dev_err=err)
     f_verify = lambda i: gdn.verify_k(geom, pools[i % len(pools)], vx, va, vb, cw, vslot, snap, vo, dev_err=err)
     f_rollback = lambda i: gdn.rollback(geom, pools[i % len(pools)], snap, vslot, vacc, dev_err=err)
